@@ -1,0 +1,139 @@
+/*
+ * convrot.h -- C-ABI of libconvrot, the ConvRot quantized linear layer for AMD MI355X (gfx950).
+ *
+ * What the layer computes (sources are the pages this library follows):
+ *   ConvRot rotates a weight by a Hadamard transform over fixed groups of input channels before
+ *   quantizing it, which spreads outlier energy so INT8 can hold it, and the GEMM then runs on
+ *   INT8 tensor cores ("minimax-h3-nvfp4-convrot核心原理", section 四 "核心原理 3：INT8 ConvRot").
+ *   The group is 256 channels (same section, detail 3; converter flag --convrot-group-size 256 in
+ *   "Qwen3-VL-32B-...-INT8-ConvRot部署优化", section 量化转换过程), INT8 weights carry one FP32
+ *   scale per output row (--scaling_mode row there; "INT8 row-scale" in section 四), and the
+ *   W4A4 variant rotates activations and weights alike and quantizes both to 4 bits with
+ *   round-to-nearest (nvfp4-convrot page, section 五 "INT4 W4A4 ConvRot").
+ *
+ *   R       = blockdiag(H_g / sqrt(g), ...) along K, H_g the Sylvester Hadamard matrix
+ *             (H[i][j] = (-1)^popcount(i & j)), g a power of two, groups contiguous along K.
+ *   INT8:   s = max|v R| / 127 per row (fp32),  q = rint(v R / s) in [-127, 127]
+ *   INT4:   s = max|v R over a 256-group| / 7 per (row, group) (fp16), c = rint(v R / s) in [-7, 7]
+ *   linear: y[m,n] = bf16( sum_k xq[m,k] wq[n,k] * sx[m] * sw[n] + bias[n] )          (INT8)
+ *           y[m,n] = bf16( sum_j (sum_{k in group j} cx cw) * sx[m,j] * sw[n,j] + bias[n] ) (W4A4)
+ *   Because R is orthogonal, (x R)(w R)^T = x w^T, so the integer product of rotated codes
+ *   approximates x w^T.  Rounding is to nearest even; a zero row/group has scale 0, codes 0.
+ *
+ * Conventions (all entry points):
+ *   - Every matrix is row-major with K contiguous.  Weights are [N, K] = [out, in].
+ *   - Pointers named x/w/xq/wq/y/scale/bias/workspace are DEVICE pointers owned by the caller;
+ *     the library allocates and frees nothing.  Matrix pointers must be 16-byte aligned, fp32
+ *     scale/bias pointers 4-byte aligned, fp16 scale pointers 2-byte aligned.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and returns without waiting.
+ *     A fault inside a kernel surfaces at the caller's next synchronisation.
+ *   - Preconditions are checked on the host before anything is launched: a violated one returns
+ *     a non-zero status and enqueues nothing.  convrot_last_error() then describes it.
+ *   - Shapes: 0 <= M, N < 2^31; 64 <= K <= 131072 and K % 64 == 0; 1 <= group <= 256 a power of
+ *     two dividing K.  M == 0 or N == 0 is a no-op that returns CONVROT_OK.
+ *   - Inputs must be finite.  The library is stateless and thread-safe, except that one
+ *     workspace buffer must not be used by two calls that may run concurrently.
+ */
+#ifndef CONVROT_H
+#define CONVROT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum convrot_status {
+    CONVROT_OK = 0,
+    CONVROT_ERR_NULL = 1,      /* a required pointer is NULL                                   */
+    CONVROT_ERR_SHAPE = 2,     /* M, N or K out of range, K % 64 != 0, or K % group != 0         */
+    CONVROT_ERR_GROUP = 3,     /* group not a power of two in [1, 256] (INT4 requires 256)       */
+    CONVROT_ERR_ALIGN = 4,     /* a pointer violates the alignment rules above                   */
+    CONVROT_ERR_DTYPE = 5,     /* unknown dtype code                                             */
+    CONVROT_ERR_BITS = 6,      /* bits is not 8 or 4                                             */
+    CONVROT_ERR_WORKSPACE = 7, /* workspace NULL or smaller than convrot_workspace_bytes()       */
+    CONVROT_ERR_HIP = 8,       /* a HIP runtime call or kernel launch failed                     */
+    CONVROT_ERR_DEVICE = 9     /* the current device is not gfx950                               */
+} convrot_status;
+
+enum { CONVROT_DTYPE_F32 = 0, CONVROT_DTYPE_BF16 = 1 };
+
+#define CONVROT_MAX_K 131072
+
+/*
+ * Offline weight preparation: rotate each weight row by R and quantize it
+ * ("ConvRot pre-rotates the weight in fixed groups before quantization", nvfp4-convrot page,
+ * section 四; quantize from the original BF16/FP32 weight, same section, detail 1).
+ *   w        [N, K] fp32 or bf16 (w_dtype)
+ *   bits 8:  wq int8 [N, K];        w_scale fp32 [N]
+ *   bits 4:  wq uint8 [N, K/2] (two codes per byte, even k in the low nibble);
+ *            w_scale fp16 [K/256, N] (group-major: scale of row n, group j at j*N + n); group 256.
+ */
+int convrot_prepare_weight(const void *w, int w_dtype, int64_t N, int64_t K, int group, int bits, void *wq,
+                           void *w_scale, hipStream_t stream);
+
+/*
+ * Online activation quantization: rotate each token row by the same R and quantize it
+ * dynamically (one scale per token for INT8, per (token, 256-group) for INT4).  Same layouts as
+ * convrot_prepare_weight with M rows.  Exposed so one quantized input can feed several linears
+ * (for example q/k/v or gate/up projections that share an input).
+ */
+int convrot_quantize_act(const void *x, int x_dtype, int64_t M, int64_t K, int group, int bits, void *xq,
+                         void *x_scale, hipStream_t stream);
+
+/*
+ * Workspace bytes needed by convrot_linear (bits 8) / convrot_linear_w4a4 (bits 4) for this
+ * shape; 0 on invalid arguments.  The workspace must be 256-byte aligned.  It is scratch: the
+ * library initialises what it needs on the stream, so any contents are fine on entry and it holds
+ * nothing useful afterwards.  convrot_gemm_i8_i32 with M <= 16 needs the same bits-8 size.
+ */
+size_t convrot_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits);
+
+/*
+ * INT8 ConvRot linear: y = bf16( (xq . wq^T) * sx[m] * sw[n] + bias[n] )   (nvfp4-convrot page,
+ * section 四: INT8 row-scale weights with ConvRot metadata on the INT8 tensor-core path).
+ *   x        bf16/fp32 [M, K] (x_dtype): rotated and quantized into the workspace first; or
+ *   x = NULL: use the caller's xq int8 [M, K] and x_scale fp32 [M] from convrot_quantize_act.
+ *   wq, w_scale from convrot_prepare_weight(bits = 8); bias fp32 [N] or NULL; y bf16 [M, N].
+ * M <= 16 runs the weight-streaming split-K GEMV, larger M the MFMA GEMM.
+ */
+int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_scale, int64_t M, int64_t N,
+                   int64_t K, int group, const int8_t *wq, const float *w_scale, const float *bias, void *y,
+                   void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * W4A4 ConvRot linear (nvfp4-convrot page, section 五): both operands rotated, INT4 per
+ * (row, 256-group) with fp16 scales, per-group integer dot products scaled and summed in fp32.
+ *   x bf16/fp32 [M, K] quantized into the workspace, or x = NULL and the caller's
+ *   xq uint8 [M, K/2] / x_scale fp16 [K/256, M] from convrot_quantize_act(bits = 4).
+ *   wq uint8 [N, K/2], w_scale fp16 [K/256, N] from convrot_prepare_weight(bits = 4).
+ *   group must be 256, K % 256 == 0, N % 8 == 0.  bias fp32 [N] or NULL; y bf16 [M, N].
+ */
+int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uint16_t *x_scale, int64_t M,
+                        int64_t N, int64_t K, int group, const uint8_t *wq, const uint16_t *w_scale,
+                        const float *bias, void *y, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Integer core without scales, for exactness checks: acc int32 [M, N] = xq . wq^T (same kernels
+ * and M-based dispatch as convrot_linear; the M <= 16 path needs the workspace).
+ */
+int convrot_gemm_i8_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K, int32_t *acc,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* W4A4 integer core without scales: acc int32 [M, N] = sum_k cx[m,k] * cw[n,k] over packed codes. */
+int convrot_gemm_i4_i32(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N, int64_t K, int32_t *acc,
+                        hipStream_t stream);
+
+/* Description of the last non-OK status returned on the calling thread ("" if none). */
+const char *convrot_last_error(void);
+
+/* Static name of a status code. */
+const char *convrot_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVROT_H */

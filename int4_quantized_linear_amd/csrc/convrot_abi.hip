@@ -1,0 +1,302 @@
+// convrot_abi.hip -- host side of the libconvrot C-ABI: argument validation, dispatch by
+// shape, workspace layout and error reporting.  Every precondition is checked before the first
+// HIP call, so a rejected call enqueues nothing.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "../../include/convrot.h"
+#include "launchers.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = std::string(convrot_status_string(code)) + ": " + buf;
+    return code;
+}
+
+bool pow2_group(int g) { return g >= 1 && g <= 256 && (g & (g - 1)) == 0; }
+int log2i(int g)
+{
+    int l = 0;
+    while ((1 << l) < g) ++l;
+    return l;
+}
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int check_shape(int64_t M, int64_t N, int64_t K, int group)
+{
+    if (M < 0 || N < 0 || M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
+        return fail(CONVROT_ERR_SHAPE, "M=%lld N=%lld must be in [0, 2^31)", (long long)M, (long long)N);
+    if (K < 64 || K > CONVROT_MAX_K || K % 64)
+        return fail(CONVROT_ERR_SHAPE, "K=%lld must be a multiple of 64 in [64, %d]", (long long)K, CONVROT_MAX_K);
+    if (!pow2_group(group)) return fail(CONVROT_ERR_GROUP, "group=%d must be a power of two in [1, 256]", group);
+    if (K % group) return fail(CONVROT_ERR_SHAPE, "K=%lld is not a multiple of group=%d", (long long)K, group);
+    return CONVROT_OK;
+}
+
+// One cached answer per device: is it gfx950?
+int check_device()
+{
+    static std::mutex mu;
+    static int known[64];   // 0 unknown, 1 ok, 2 wrong arch
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(CONVROT_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(CONVROT_ERR_DEVICE, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lk(mu);
+    if (!known[dev]) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return fail(CONVROT_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        known[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        if (known[dev] == 2) return fail(CONVROT_ERR_DEVICE, "device %d is %s, libconvrot is built for gfx950", dev, prop.gcnArchName);
+    }
+    return known[dev] == 1 ? CONVROT_OK : fail(CONVROT_ERR_DEVICE, "device %d is not gfx950", dev);
+}
+
+int hip_status(hipError_t e, const char *what)
+{
+    return e == hipSuccess ? CONVROT_OK : fail(CONVROT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Zero-fill of a small device region (a kernel rather than hipMemsetAsync so that a captured
+// graph replays it correctly).
+__global__ void fill_zero_kernel(uint4 *p, size_t n16)
+{
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t zero_region(void *p, size_t bytes, hipStream_t s)
+{
+    const size_t n16 = (bytes + 15) / 16;
+    if (!n16) return hipSuccess;
+    unsigned blocks = (unsigned)((n16 + 255) / 256);
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, s, static_cast<uint4 *>(p), n16);
+    return hipGetLastError();
+}
+
+// Workspace layout, each region 256-byte aligned:
+//   bits 8: [split-K accumulators + counters if M <= 16][xq int8 M*K][x_scale fp32 M]
+//   bits 4: [xq packed M*K/2][x_scale fp16 (K/256)*M]
+struct WsLayout {
+    size_t gemv = 0, xq = 0, xs = 0, total = 0;
+    size_t gemv_bytes = 0;
+};
+
+WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int bits)
+{
+    WsLayout L;
+    size_t off = 0;
+    if (bits == 8) {
+        if (M <= 16) {
+            L.gemv = off;
+            L.gemv_bytes = convrot::gemv_i8_workspace_bytes(M, N);
+            off += round256(L.gemv_bytes);
+        }
+        L.xq = off;
+        off += round256((size_t)(M * K));
+        L.xs = off;
+        off += round256((size_t)M * 4);
+    } else {
+        L.xq = off;
+        off += round256((size_t)(M * K / 2));
+        L.xs = off;
+        off += round256((size_t)(M * (K / 256) * 2));
+    }
+    L.total = off;
+    return L;
+}
+
+int quantize_common(const void *x, int dtype, int64_t R, int64_t K, int group, int bits, void *q, void *scale,
+                    hipStream_t stream, const char *who)
+{
+    if (!x || !q || !scale) return fail(CONVROT_ERR_NULL, "%s: x, q and scale must be non-NULL", who);
+    if (dtype != CONVROT_DTYPE_F32 && dtype != CONVROT_DTYPE_BF16) return fail(CONVROT_ERR_DTYPE, "%s: dtype=%d", who, dtype);
+    if (bits != 8 && bits != 4) return fail(CONVROT_ERR_BITS, "%s: bits=%d", who, bits);
+    int rc = check_shape(R, 1, K, group);
+    if (rc) return rc;
+    if (bits == 4 && (group != 256 || K % 256))
+        return fail(CONVROT_ERR_GROUP, "%s: INT4 needs group 256 and K %% 256 == 0 (group=%d, K=%lld)", who, group, (long long)K);
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, bits == 8 ? 4 : 2))
+        return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
+    if (R == 0) return CONVROT_OK;
+    if ((rc = check_device())) return rc;
+    return hip_status(convrot::launch_rotate_quant(x, dtype == CONVROT_DTYPE_F32, R, (int)K, log2i(group), bits, q,
+                                                   scale, stream),
+                      who);
+}
+
+} // namespace
+
+extern "C" {
+
+const char *convrot_status_string(int s)
+{
+    switch (s) {
+    case CONVROT_OK: return "CONVROT_OK";
+    case CONVROT_ERR_NULL: return "CONVROT_ERR_NULL";
+    case CONVROT_ERR_SHAPE: return "CONVROT_ERR_SHAPE";
+    case CONVROT_ERR_GROUP: return "CONVROT_ERR_GROUP";
+    case CONVROT_ERR_ALIGN: return "CONVROT_ERR_ALIGN";
+    case CONVROT_ERR_DTYPE: return "CONVROT_ERR_DTYPE";
+    case CONVROT_ERR_BITS: return "CONVROT_ERR_BITS";
+    case CONVROT_ERR_WORKSPACE: return "CONVROT_ERR_WORKSPACE";
+    case CONVROT_ERR_HIP: return "CONVROT_ERR_HIP";
+    case CONVROT_ERR_DEVICE: return "CONVROT_ERR_DEVICE";
+    default: return "CONVROT_ERR_UNKNOWN";
+    }
+}
+
+const char *convrot_last_error(void) { return g_last_error.c_str(); }
+
+int convrot_prepare_weight(const void *w, int w_dtype, int64_t N, int64_t K, int group, int bits, void *wq,
+                           void *w_scale, hipStream_t stream)
+{
+    return quantize_common(w, w_dtype, N, K, group, bits, wq, w_scale, stream, "convrot_prepare_weight");
+}
+
+int convrot_quantize_act(const void *x, int x_dtype, int64_t M, int64_t K, int group, int bits, void *xq,
+                         void *x_scale, hipStream_t stream)
+{
+    return quantize_common(x, x_dtype, M, K, group, bits, xq, x_scale, stream, "convrot_quantize_act");
+}
+
+size_t convrot_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits)
+{
+    if (M < 0 || N < 0 || K <= 0 || (bits != 8 && bits != 4)) return 0;
+    return ws_layout(M, N, K, bits).total;
+}
+
+int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_scale, int64_t M, int64_t N,
+                   int64_t K, int group, const int8_t *wq, const float *w_scale, const float *bias, void *y,
+                   void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const char *who = "convrot_linear";
+    int rc = check_shape(M, N, K, group);
+    if (rc) return rc;
+    if (!wq || !w_scale || !y) return fail(CONVROT_ERR_NULL, "%s: wq, w_scale and y must be non-NULL", who);
+    if (!x && (!xq || !x_scale)) return fail(CONVROT_ERR_NULL, "%s: give x, or both xq and x_scale", who);
+    if (x && x_dtype != CONVROT_DTYPE_F32 && x_dtype != CONVROT_DTYPE_BF16)
+        return fail(CONVROT_ERR_DTYPE, "%s: x_dtype=%d", who, x_dtype);
+    if ((x && !aligned(x, 16)) || (!x && (!aligned(xq, 16) || !aligned(x_scale, 4))) || !aligned(wq, 16) ||
+        !aligned(w_scale, 4) || !aligned(y, 16) || (bias && !aligned(bias, 4)))
+        return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
+    const WsLayout L = ws_layout(M, N, K, 8);
+    const bool need_ws = x != nullptr || M <= 16;
+    if (need_ws && (!workspace || workspace_bytes < L.total || !aligned(workspace, 256)))
+        return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes (got %zu)", who, L.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (M == 0 || N == 0) return CONVROT_OK;
+    if ((rc = check_device())) return rc;
+
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    if (M <= 16 && (rc = hip_status(zero_region(ws + L.gemv, L.gemv_bytes, stream), "zero split-K workspace")))
+        return rc;
+    if (x) {
+        int8_t *qx = reinterpret_cast<int8_t *>(ws + L.xq);
+        float *sx = reinterpret_cast<float *>(ws + L.xs);
+        rc = hip_status(convrot::launch_rotate_quant(x, x_dtype == CONVROT_DTYPE_F32, M, (int)K, log2i(group), 8, qx,
+                                                     sx, stream),
+                        "rotate_quant");
+        if (rc) return rc;
+        xq = qx;
+        x_scale = sx;
+    }
+    hipError_t e = M <= 16 ? convrot::launch_gemv_i8(xq, wq, x_scale, w_scale, bias, y, convrot::Epi::Bf16, M, N,
+                                                      (int)K, ws + L.gemv, stream)
+                           : convrot::launch_gemm_i8(xq, wq, x_scale, w_scale, bias, y, convrot::Epi::Bf16, M, N,
+                                                      (int)K, stream);
+    return hip_status(e, M <= 16 ? "gemv_i8" : "gemm_i8");
+}
+
+int convrot_gemm_i8_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K, int32_t *acc,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const char *who = "convrot_gemm_i8_i32";
+    int rc = check_shape(M, N, K, 1);
+    if (rc) return rc;
+    if (!xq || !wq || !acc) return fail(CONVROT_ERR_NULL, "%s: xq, wq and acc must be non-NULL", who);
+    if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(acc, 16)) return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
+    const size_t need = M <= 16 ? round256(convrot::gemv_i8_workspace_bytes(M, N)) : 0;
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+        return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes", who, need);
+    if (M == 0 || N == 0) return CONVROT_OK;
+    if ((rc = check_device())) return rc;
+    if (M <= 16) {
+        if ((rc = hip_status(zero_region(workspace, need, stream), "zero split-K workspace"))) return rc;
+        return hip_status(convrot::launch_gemv_i8(xq, wq, nullptr, nullptr, nullptr, acc, convrot::Epi::Int32, M, N,
+                                                  (int)K, workspace, stream),
+                          "gemv_i8");
+    }
+    return hip_status(
+        convrot::launch_gemm_i8(xq, wq, nullptr, nullptr, nullptr, acc, convrot::Epi::Int32, M, N, (int)K, stream),
+        "gemm_i8");
+}
+
+int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uint16_t *x_scale, int64_t M,
+                        int64_t N, int64_t K, int group, const uint8_t *wq, const uint16_t *w_scale,
+                        const float *bias, void *y, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const char *who = "convrot_linear_w4a4";
+    int rc = check_shape(M, N, K, group);
+    if (rc) return rc;
+    if (group != 256 || K % 256) return fail(CONVROT_ERR_GROUP, "%s: W4A4 needs group 256 and K %% 256 == 0", who);
+    if (N % 8) return fail(CONVROT_ERR_SHAPE, "%s: N=%lld must be a multiple of 8", who, (long long)N);
+    if (!wq || !w_scale || !y) return fail(CONVROT_ERR_NULL, "%s: wq, w_scale and y must be non-NULL", who);
+    if (!x && (!xq || !x_scale)) return fail(CONVROT_ERR_NULL, "%s: give x, or both xq and x_scale", who);
+    if (x && x_dtype != CONVROT_DTYPE_F32 && x_dtype != CONVROT_DTYPE_BF16)
+        return fail(CONVROT_ERR_DTYPE, "%s: x_dtype=%d", who, x_dtype);
+    if ((x && !aligned(x, 16)) || (!x && (!aligned(xq, 16) || !aligned(x_scale, 2))) || !aligned(wq, 16) ||
+        !aligned(w_scale, 8) || !aligned(y, 16) || (bias && !aligned(bias, 4)))
+        return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer (w_scale needs 8 bytes)", who);
+    const WsLayout L = ws_layout(M, N, K, 4);
+    if (x && (!workspace || workspace_bytes < L.total || !aligned(workspace, 256)))
+        return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes", who, L.total);
+    if (M == 0 || N == 0) return CONVROT_OK;
+    if ((rc = check_device())) return rc;
+    if (x) {
+        uint8_t *ws = static_cast<uint8_t *>(workspace);
+        rc = hip_status(convrot::launch_rotate_quant(x, x_dtype == CONVROT_DTYPE_F32, M, (int)K, 8, 4, ws + L.xq,
+                                                     ws + L.xs, stream),
+                        "rotate_quant");
+        if (rc) return rc;
+        xq = ws + L.xq;
+        x_scale = reinterpret_cast<const uint16_t *>(ws + L.xs);
+    }
+    return hip_status(convrot::launch_gemm_w4a4(xq, wq, x_scale, w_scale, bias, y, convrot::Epi::Bf16, M, N, (int)K,
+                                                stream),
+                      "gemm_w4a4");
+}
+
+int convrot_gemm_i4_i32(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N, int64_t K, int32_t *acc,
+                        hipStream_t stream)
+{
+    const char *who = "convrot_gemm_i4_i32";
+    int rc = check_shape(M, N, K, 256);
+    if (rc) return rc;
+    if (K % 256 || N % 8) return fail(CONVROT_ERR_SHAPE, "%s: needs K %% 256 == 0 and N %% 8 == 0", who);
+    if (!xq || !wq || !acc) return fail(CONVROT_ERR_NULL, "%s: xq, wq and acc must be non-NULL", who);
+    if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(acc, 16)) return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
+    if (M == 0 || N == 0) return CONVROT_OK;
+    if ((rc = check_device())) return rc;
+    return hip_status(
+        convrot::launch_gemm_w4a4(xq, wq, nullptr, nullptr, nullptr, acc, convrot::Epi::Int32, M, N, (int)K, stream),
+        "gemm_w4a4");
+}
+
+} // extern "C"

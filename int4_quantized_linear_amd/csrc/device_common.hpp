@@ -1,0 +1,80 @@
+// device_common.hpp -- small gfx950 device helpers shared by the ConvRot HIP kernels.
+// Internal to libconvrot; not part of the public C-ABI.
+#pragma once
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convrot {
+
+constexpr int kWave = 64;                 // CDNA wavefront width
+constexpr float kMagicRound = 12582912.0f; // 1.5 * 2^23: adding it leaves round-to-nearest-even(x) in the low mantissa bits
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32); a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    v2bf16 r;
+    r[0] = (__bf16)a;
+    r[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t d) { return __uint_as_float(d & 0xffff0000u); }
+
+// Lane exchanges inside a quad (DPP quad_perm), all lanes enabled.
+__device__ __forceinline__ float dpp_xor1(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)); // [1,0,3,2]
+}
+__device__ __forceinline__ float dpp_xor2(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)); // [2,3,0,1]
+}
+
+// Exchange the upper 32 lanes of `a` with the lower 32 lanes of `b` (v_permlane32_swap):
+// afterwards a = [a_lo | b_lo], b = [a_hi | b_hi].
+__device__ __forceinline__ void swap32(uint32_t &a, uint32_t &b)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
+__device__ __forceinline__ void swap32f(float &a, float &b)
+{
+    uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+    swap32(ua, ub);
+    a = __uint_as_float(ua);
+    b = __uint_as_float(ub);
+}
+
+// Round-to-nearest-even of x*m with a single rounding; the signed integer sits in the low
+// bits of the returned float's bit pattern (valid for |x*m| < 2^22).
+__device__ __forceinline__ uint32_t rne_bits(float x, float m) { return __float_as_uint(__builtin_fmaf(x, m, kMagicRound)); }
+
+// Low bytes of four rne_bits() results -> one packed dword (byte 0 = t0).
+__device__ __forceinline__ uint32_t pack4_i8(uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3)
+{
+    uint32_t p01 = __builtin_amdgcn_perm(t1, t0, 0x0c0c0400u);
+    uint32_t p23 = __builtin_amdgcn_perm(t3, t2, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+}
+
+// Low nibbles of eight rne_bits() results -> one dword (nibble i = t[i]).
+__device__ __forceinline__ uint32_t pack8_i4(const uint32_t *t)
+{
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r |= (t[i] & 0xFu) << (4 * i);
+    return r;
+}
+
+} // namespace convrot

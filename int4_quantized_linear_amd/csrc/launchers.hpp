@@ -1,0 +1,33 @@
+// launchers.hpp -- internal host launchers of the ConvRot HIP kernels (not the public ABI).
+// Every launcher assumes its arguments were validated by the C-ABI layer and only returns
+// the launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convrot {
+
+// Rotate rows of x (bf16 or fp32, [rows, K]) by the grouped Hadamard and quantize:
+// bits 8 -> q int8 [rows, K], scale fp32 [rows]; bits 4 -> q uint8 [rows, K/2], scale fp16 [rows, K/256].
+hipError_t launch_rotate_quant(const void *x, bool x_f32, int64_t rows, int K, int log2g, int bits, void *q,
+                               void *scale, hipStream_t stream);
+
+// Epilogue selector of the integer GEMM / GEMV kernels.
+enum class Epi { Bf16 = 0, Int32 = 1 };
+
+// y[M,N] = bf16(acc * sx[m] * sw[n] + bias[n])  or  acc32[M,N] = acc,   acc = xq . wq^T  (M > 16).
+hipError_t launch_gemm_i8(const int8_t *xq, const int8_t *wq, const float *sx, const float *sw, const float *bias,
+                          void *y, Epi epi, int64_t M, int64_t N, int K, hipStream_t stream);
+
+// Same contraction for M <= 16 (weight streaming, split-K).  `ws` holds M*N int32 partial sums
+// followed by ceil(N/64) counters and must be zero on entry (gemv_i8_workspace_bytes bytes).
+size_t gemv_i8_workspace_bytes(int64_t M, int64_t N);
+hipError_t launch_gemv_i8(const int8_t *xq, const int8_t *wq, const float *sx, const float *sw, const float *bias,
+                          void *y, Epi epi, int64_t M, int64_t N, int K, void *ws, hipStream_t stream);
+
+// W4A4: y = bf16(sum_g acc_g * sx[m,g] * sw[n,g] + bias[n]) with packed int4 operands and
+// fp16 group scales (group = 256), or the unscaled int32 total sum_k cx*cw (scales ignored).
+hipError_t launch_gemm_w4a4(const uint8_t *xq, const uint8_t *wq, const uint16_t *sx, const uint16_t *sw,
+                            const float *bias, void *y, Epi epi, int64_t M, int64_t N, int K, hipStream_t stream);
+
+} // namespace convrot

@@ -1,0 +1,73 @@
+"""Comparison rules between the HIP path and the CPU oracle.
+
+(a) quantized codes: |delta| <= 1 LSB everywhere, mismatch rate <= 1e-4 (fp32 rotation sums may
+    round differently from the oracle's fp64 sums right at a rounding edge);
+(b) integer accumulators, given identical codes: bit-exact;
+(c) fp32 scales: within 1e-6 relative.  fp16 group scales are themselves values rounded in
+    floating point, so they must be equal except where the fp32 group max differs by rounding:
+    at most 1 fp16 ulp apart, at a mismatch rate <= 1e-3;
+(d) bf16 output: max|y_gpu - y_oracle| / max|y_oracle| <= 1e-2, against the oracle's quantized
+    result (not the exact product), plus a tighter check that almost every element is within a
+    couple of bf16 ulps of it.
+"""
+import sys
+
+import numpy as np
+import torch
+
+CODE_MISMATCH_RATE = 1e-4
+SCALE_RTOL = 1e-6
+F16_SCALE_MISMATCH_RATE = 1e-3
+Y_REL_TOL = 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_np64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_codes(gpu: np.ndarray, ref: np.ndarray, what: str = "codes", rate: float = CODE_MISMATCH_RATE):
+    gpu = gpu.astype(np.int64)
+    ref = ref.astype(np.int64)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    d = np.abs(gpu - ref)
+    mism = np.count_nonzero(d)
+    assert d.max(initial=0) <= 1, "%s: max |delta| = %d" % (what, d.max())
+    assert mism <= rate * d.size, "%s: %d mismatches of %d (rate %.2e)" % (what, mism, d.size, mism / max(d.size, 1))
+    return mism
+
+
+def check_scales_f32(gpu: np.ndarray, ref: np.ndarray, what: str = "scales"):
+    gpu = gpu.astype(np.float64)
+    ref = ref.astype(np.float64)
+    err = np.abs(gpu - ref)
+    bad = err > SCALE_RTOL * np.abs(ref)
+    assert not bad.any(), "%s: %d scales off by more than %g relative (max rel %.3e)" % (
+        what, bad.sum(), SCALE_RTOL, (err / np.maximum(np.abs(ref), 1e-300)).max())
+
+
+def check_scales_f16(gpu: np.ndarray, ref: np.ndarray, what: str = "fp16 scales"):
+    g = gpu.astype(np.float16).view(np.uint16).astype(np.int64)
+    r = ref.astype(np.float16).view(np.uint16).astype(np.int64)
+    d = np.abs(g - r)
+    assert d.max(initial=0) <= 1, "%s: scales differ by %d fp16 ulps" % (what, d.max())
+    mism = np.count_nonzero(d)
+    assert mism <= max(1, F16_SCALE_MISMATCH_RATE * d.size), "%s: %d of %d differ" % (what, mism, d.size)
+    return mism
+
+
+def check_y(gpu: np.ndarray, ref: np.ndarray, what: str = "y", strict_frac: float = 1e-3):
+    gpu = gpu.astype(np.float64)
+    ref = ref.astype(np.float64)
+    scale = np.abs(ref).max()
+    err = np.abs(gpu - ref)
+    rel = err.max() / scale if scale > 0 else err.max()
+    assert rel <= Y_REL_TOL, "%s: max error %.3e of max|y| (tol %g)" % (what, rel, Y_REL_TOL)
+    # bf16 has 8 significant bits: rounding alone gives <= 2^-9 |y|; allow 4 ulps + a tiny floor
+    loose = err > (2.0 ** -6) * np.abs(ref) + 1e-4 * scale
+    assert loose.mean() <= strict_frac, "%s: %d of %d elements beyond 4 bf16 ulps" % (what, loose.sum(), loose.size)
+    return rel

@@ -1,0 +1,259 @@
+"""HIP path vs CPU oracle, element by element, on seeded inputs (rules in tests/parity.py).
+
+Sizes are chosen so the oracle finishes in seconds while the kernels still run several tiles
+plus ragged tails; the full-size workloads are checked on sampled rows / outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+from int4_quantized_linear_amd import workloads
+from oracle import oracle as orc
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def cr():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from int4_quantized_linear_amd import convrot
+    convrot.load()
+    return convrot
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _x64(t):
+    return P.to_np64(t)
+
+
+# ------------------------------------------------------------------ rotate + quantize (INT8)
+
+QUANT_CASES = [
+    # rows, K, g, dtype
+    (4, 512, 256, torch.float32),
+    (37, 320, 64, torch.bfloat16),
+    (37, 320, 1, torch.bfloat16),
+    (29, 320, 8, torch.float32),
+    (64, 768, 128, torch.bfloat16),
+    (65, 768, 32, torch.bfloat16),
+    (300, 5376, 256, torch.bfloat16),
+    (12, 5120, 256, torch.bfloat16),
+    (5, 25600, 256, torch.bfloat16),
+    (3, 40960, 256, torch.bfloat16),
+    (2, 131072, 256, torch.bfloat16),
+    (130, 2688, 128, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("rows,K,g,dtype", QUANT_CASES)
+def test_quantize_int8_parity(cr, rows, K, g, dtype):
+    P.say("quantize_act int8 rows=%d K=%d g=%d %s" % (rows, K, g, dtype))
+    x, _, _ = workloads.ragged_case(rows, K, 8, seed=rows + K + g, dtype=dtype)
+    q, s = cr.quantize_act(x.to(DEV), group=g, bits=8)
+    torch.cuda.synchronize()
+    qr, sr = orc.quantize_act_i8(_x64(x), g)
+    P.check_scales_f32(_np(s), sr)
+    P.check_codes(_np(q), qr)
+
+
+def test_quantize_zero_rows_and_single_outlier(cr):
+    x = torch.zeros(6, 512)
+    x[1, 7] = 1000.0
+    x[3] = torch.linspace(-1, 1, 512)
+    x[4, :] = 1e-3
+    q, s = cr.quantize_act(x.to(DEV), group=256, bits=8)
+    torch.cuda.synchronize()
+    qr, sr = orc.quantize_act_i8(x.double().numpy(), 256)
+    assert _np(s)[0] == 0 and np.all(_np(q)[0] == 0)
+    P.check_scales_f32(_np(s), sr)
+    P.check_codes(_np(q), qr, rate=0.0)
+
+
+def test_prepare_weight_same_as_quantize_act(cr):
+    w = workloads.gaussian_weights(300, 768, cfg=99)
+    a = cr.prepare_weight(w.to(DEV), 256, 8)
+    b = cr.quantize_act(w.to(DEV), 256, 8)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------ integer core (rule b)
+
+GEMM_CASES = [
+    # M, N, K  (M <= 16 runs the split-K GEMV kernel)
+    (1, 64, 64), (12, 1000, 5120), (16, 264, 320), (12, 8192, 5120), (3, 5120, 25600),
+    (17, 8, 64), (300, 264, 320), (513, 1000, 5376), (256, 256, 128), (1000, 1280, 1024),
+]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_CASES)
+def test_gemm_i32_bit_exact(cr, M, N, K):
+    P.say("gemm_i8_i32 M=%d N=%d K=%d" % (M, N, K))
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    a = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    b = rng.integers(-127, 128, size=(N, K), dtype=np.int8)
+    acc = cr.gemm_i8_i32(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV))
+    torch.cuda.synchronize()
+    ref = orc.gemm_i32(a, b)
+    assert np.array_equal(_np(acc), ref)
+
+
+def test_gemm_i32_extreme_values(cr):
+    """All-(+-127) operands reach the largest accumulators."""
+    M, N, K = 40, 72, 5376
+    a = np.full((M, K), 127, np.int8)
+    a[1::2] = -127
+    b = np.full((N, K), -127, np.int8)
+    acc = cr.gemm_i8_i32(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(acc), orc.gemm_i32(a, b))
+    assert abs(int(_np(acc)[0, 0])) == 127 * 127 * K
+
+
+# ------------------------------------------------------------------ full INT8 linear (rules a-d)
+
+def _linear_case(cr, x, w, b, g):
+    xd, wd = x.to(DEV), w.to(DEV)
+    bd = None if b is None else b.to(DEV)
+    wq, ws = cr.prepare_weight(wd, g, 8)
+    y = cr.linear(xd, wq, ws, bd, group=g)
+    xq, xs = cr.quantize_act(xd, g, 8)
+    y2 = cr.linear(None, wq, ws, bd, group=g, xq=xq, x_scale=xs)
+    torch.cuda.synchronize()
+    ref = orc.linear_w8a8(_x64(x), _x64(w), None if b is None else b.numpy(), g)
+    P.check_codes(_np(wq), ref["qw"], "qw")
+    P.check_scales_f32(_np(ws), ref["sw"], "sw")
+    P.check_codes(_np(xq), ref["qx"], "qx")
+    P.check_scales_f32(_np(xs), ref["sx"], "sx")
+    P.check_y(_x64(y), ref["y"])
+    assert torch.equal(y, y2), "pre-quantized path differs from the fused path"
+    return y, ref
+
+
+def test_linear_tiny_config(cr):
+    x, w = workloads.tiny_inputs()
+    _linear_case(cr, x, w, None, 256)
+    b = torch.from_numpy(np.linspace(-1, 1, 256).astype(np.float32))
+    _linear_case(cr, x, w, b, 256)
+
+
+LINEAR_CASES = [
+    (12, 1000, 320, 64), (16, 1024, 5120, 256), (1, 200, 512, 256), (17, 264, 320, 32),
+    (300, 1000, 768, 128), (257, 520, 1024, 256), (600, 264, 2688, 128),
+]
+
+
+@pytest.mark.parametrize("M,N,K,g", LINEAR_CASES)
+def test_linear_ragged(cr, M, N, K, g):
+    P.say("linear M=%d N=%d K=%d g=%d" % (M, N, K, g))
+    x, w, b = workloads.ragged_case(M, K, N, seed=3)
+    _linear_case(cr, x, w, b, g)
+
+
+@pytest.mark.parametrize("K,N", workloads.DECODE_SHAPES)
+def test_linear_decode_shapes(cr, K, N):
+    P.say("decode linear M=12 K=%d N=%d" % (K, N))
+    x, w = workloads.decode_inputs(K, N)
+    _linear_case(cr, x, w, None, 256)
+
+
+def test_linear_prefill_full_size_sampled(cr):
+    """Full 4096 x 5376 x 16128 workload; oracle on 384 sampled token rows / weight rows and
+    4096 sampled outputs."""
+    M, K, N = workloads.PREFILL["M"], workloads.PREFILL["K"], workloads.PREFILL["N"]
+    x, w, b = workloads.prefill_inputs()
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    wq, ws = cr.prepare_weight(wd, 256, 8)
+    y = cr.linear(xd, wq, ws, bd, group=256)
+    xq, xs = cr.quantize_act(xd, 256, 8)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    mr = np.sort(rng.choice(M, 384, replace=False))
+    nr = np.sort(rng.choice(N, 384, replace=False))
+    qx, sx = orc.quantize_act_i8(_x64(x[mr]), 256)
+    qw, sw = orc.prepare_weight_i8(_x64(w[nr]), 256)
+    P.check_codes(_np(xq)[mr], qx, "qx rows")
+    P.check_scales_f32(_np(xs)[mr], sx, "sx rows")
+    P.check_codes(_np(wq)[nr], qw, "qw rows")
+    P.check_scales_f32(_np(ws)[nr], sw, "sw rows")
+    ii = rng.integers(0, 384, 4096)
+    jj = rng.integers(0, 384, 4096)
+    acc = orc.gemm_i32_pairs(qx, qw, ii, jj)
+    yref = acc.astype(np.float64) * sx[ii].astype(np.float64) * sw[jj].astype(np.float64) + b.numpy()[nr[jj]]
+    ygpu = _x64(y)[mr[ii], nr[jj]]
+    P.check_y(ygpu, yref, "sampled y")
+    # integer core at full size on the GPU's own codes for the same pairs
+    accg = _np(cr.gemm_i8_i32(xq, wq))
+    assert np.array_equal(accg[mr[ii], nr[jj]], orc.gemm_i32_pairs(_np(xq), _np(wq), mr[ii], nr[jj]))
+
+
+def test_linear_empty_and_repeat(cr):
+    w = workloads.gaussian_weights(64, 256, cfg=98).to(DEV)
+    wq, ws = cr.prepare_weight(w, 256, 8)
+    y = cr.linear(torch.empty(0, 256, dtype=torch.bfloat16, device=DEV), wq, ws)
+    assert y.shape == (0, 64)
+    # two decode calls in a row with different inputs reuse the split-K workspace correctly
+    for seed in (1, 2):
+        x = workloads.heavy_tailed_acts(12, 256, cfg=98, layer=seed).to(DEV)
+        y = cr.linear(x, wq, ws)
+        torch.cuda.synchronize()
+        ref = orc.linear_w8a8(_x64(x), _x64(w), None, 256)
+        P.check_y(_x64(y), ref["y"])
+
+
+# ------------------------------------------------------------------ W4A4
+
+W4_QUANT_CASES = [(4, 512), (37, 768), (300, 5376), (12, 25600)]
+
+
+@pytest.mark.parametrize("rows,K", W4_QUANT_CASES)
+def test_quantize_int4_parity(cr, rows, K):
+    P.say("quantize int4 rows=%d K=%d" % (rows, K))
+    x, _, _ = workloads.ragged_case(rows, K, 8, seed=rows + K)
+    q, s = cr.quantize_act(x.to(DEV), 256, 4)
+    torch.cuda.synchronize()
+    c, sr, pr = orc.prepare_i4(_x64(x), 256)
+    P.check_scales_f16(_np(s).T, sr)
+    P.check_codes(orc.unpack_i4(_np(q)), c, "int4 codes", rate=1e-3)
+
+
+W4_GEMM_CASES = [(17, 256, 256), (130, 264, 512), (300, 520, 5376), (1, 8, 256)]
+
+
+@pytest.mark.parametrize("M,N,K", W4_GEMM_CASES)
+def test_gemm_i4_bit_exact(cr, M, N, K):
+    P.say("gemm_i4_i32 M=%d N=%d K=%d" % (M, N, K))
+    rng = np.random.default_rng(M + N + K)
+    cx = rng.integers(-8, 8, size=(M, K), dtype=np.int8)
+    cw = rng.integers(-8, 8, size=(N, K), dtype=np.int8)
+    acc = cr.gemm_i4_i32(torch.from_numpy(orc.pack_i4(cx)).to(DEV), torch.from_numpy(orc.pack_i4(cw)).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(acc), orc.gemm_i32(cx, cw))
+
+
+W4_LINEAR_CASES = [(4, 256, 512), (130, 264, 768), (257, 1024, 5376), (12, 1024, 5120)]
+
+
+@pytest.mark.parametrize("M,N,K", W4_LINEAR_CASES)
+def test_linear_w4a4_parity(cr, M, N, K):
+    P.say("linear_w4a4 M=%d N=%d K=%d" % (M, N, K))
+    x, w, b = workloads.ragged_case(M, K, N, seed=5)
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    wq, ws = cr.prepare_weight(wd, 256, 4)
+    y = cr.linear_w4a4(xd, wq, ws, bd)
+    xq, xs = cr.quantize_act(xd, 256, 4)
+    torch.cuda.synchronize()
+    ref = orc.linear_w4a4(_x64(x), _x64(w), b.numpy(), 256)
+    P.check_scales_f16(_np(ws).T, ref["sw"], "sw16")
+    P.check_scales_f16(_np(xs).T, ref["sx"], "sx16")
+    # y against the oracle evaluated on the GPU's own codes and scales (exact integer part) ...
+    yown = orc.linear_i4(orc.unpack_i4(_np(xq)), _np(xs).T, orc.unpack_i4(_np(wq)), _np(ws).T, b.numpy(), 256)
+    P.check_y(_x64(y), yown, "y (own codes)", strict_frac=1e-4)
+    # ... and against the oracle end to end
+    P.check_y(_x64(y), ref["y"], "y (oracle codes)", strict_frac=2e-2)
