@@ -72,26 +72,8 @@ int hip_status(hipError_t e, const char *what)
     return e == hipSuccess ? CONVROT_OK : fail(CONVROT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Zero-fill of a small device region (a kernel rather than hipMemsetAsync so that a captured
-// graph replays it correctly).
-__global__ void fill_zero_kernel(uint4 *p, size_t n16)
-{
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
-        p[i] = make_uint4(0, 0, 0, 0);
-}
-
-hipError_t zero_region(void *p, size_t bytes, hipStream_t s)
-{
-    const size_t n16 = (bytes + 15) / 16;
-    if (!n16) return hipSuccess;
-    unsigned blocks = (unsigned)((n16 + 255) / 256);
-    if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, s, static_cast<uint4 *>(p), n16);
-    return hipGetLastError();
-}
-
-// Workspace layout, each region 256-byte aligned:
-//   bits 8: [split-K accumulators + counters if M <= 16][xq int8 M*K][x_scale fp32 M]
+// Workspace layout, each region 256-byte aligned; all of it is scratch (no initial contents):
+//   bits 8: [split-K counters + partial sums if M <= 16][xq int8 M*K][x_scale fp32 M]
 //   bits 4: [xq packed M*K/2][x_scale fp16 (K/256)*M]
 struct WsLayout {
     size_t gemv = 0, xq = 0, xs = 0, total = 0;
@@ -105,7 +87,7 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int bits)
     if (bits == 8) {
         if (M <= 16) {
             L.gemv = off;
-            L.gemv_bytes = convrot::gemv_i8_workspace_bytes(M, N);
+            L.gemv_bytes = convrot::gemv_i8_workspace_bytes(M, N, (int)K);
             off += round256(L.gemv_bytes);
         }
         L.xq = off;
@@ -125,6 +107,8 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int bits)
 int quantize_common(const void *x, int dtype, int64_t R, int64_t K, int group, int bits, void *q, void *scale,
                     hipStream_t stream, const char *who)
 {
+    if (R == 0 && K >= 64 && K <= CONVROT_MAX_K && K % 64 == 0 && pow2_group(group) && K % group == 0)
+        return CONVROT_OK;   // empty input: nothing to read or write
     if (!x || !q || !scale) return fail(CONVROT_ERR_NULL, "%s: x, q and scale must be non-NULL", who);
     if (dtype != CONVROT_DTYPE_F32 && dtype != CONVROT_DTYPE_BF16) return fail(CONVROT_ERR_DTYPE, "%s: dtype=%d", who, dtype);
     if (bits != 8 && bits != 4) return fail(CONVROT_ERR_BITS, "%s: bits=%d", who, bits);
@@ -189,6 +173,7 @@ int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_
     const char *who = "convrot_linear";
     int rc = check_shape(M, N, K, group);
     if (rc) return rc;
+    if (M == 0 || N == 0) return CONVROT_OK;
     if (!wq || !w_scale || !y) return fail(CONVROT_ERR_NULL, "%s: wq, w_scale and y must be non-NULL", who);
     if (!x && (!xq || !x_scale)) return fail(CONVROT_ERR_NULL, "%s: give x, or both xq and x_scale", who);
     if (x && x_dtype != CONVROT_DTYPE_F32 && x_dtype != CONVROT_DTYPE_BF16)
@@ -197,7 +182,7 @@ int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_
         !aligned(w_scale, 4) || !aligned(y, 16) || (bias && !aligned(bias, 4)))
         return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
     const WsLayout L = ws_layout(M, N, K, 8);
-    const bool need_ws = x != nullptr || M <= 16;
+    const bool need_ws = x != nullptr || (M <= 16 && L.gemv_bytes > 0);
     if (need_ws && (!workspace || workspace_bytes < L.total || !aligned(workspace, 256)))
         return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes (got %zu)", who, L.total,
                     workspace ? workspace_bytes : (size_t)0);
@@ -205,8 +190,6 @@ int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_
     if ((rc = check_device())) return rc;
 
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    if (M <= 16 && (rc = hip_status(zero_region(ws + L.gemv, L.gemv_bytes, stream), "zero split-K workspace")))
-        return rc;
     if (x) {
         int8_t *qx = reinterpret_cast<int8_t *>(ws + L.xq);
         float *sx = reinterpret_cast<float *>(ws + L.xs);
@@ -230,15 +213,15 @@ int convrot_gemm_i8_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N
     const char *who = "convrot_gemm_i8_i32";
     int rc = check_shape(M, N, K, 1);
     if (rc) return rc;
+    if (M == 0 || N == 0) return CONVROT_OK;
     if (!xq || !wq || !acc) return fail(CONVROT_ERR_NULL, "%s: xq, wq and acc must be non-NULL", who);
     if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(acc, 16)) return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
-    const size_t need = M <= 16 ? round256(convrot::gemv_i8_workspace_bytes(M, N)) : 0;
+    const size_t need = M <= 16 ? round256(convrot::gemv_i8_workspace_bytes(M, N, (int)K)) : 0;
     if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
         return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes", who, need);
     if (M == 0 || N == 0) return CONVROT_OK;
     if ((rc = check_device())) return rc;
     if (M <= 16) {
-        if ((rc = hip_status(zero_region(workspace, need, stream), "zero split-K workspace"))) return rc;
         return hip_status(convrot::launch_gemv_i8(xq, wq, nullptr, nullptr, nullptr, acc, convrot::Epi::Int32, M, N,
                                                   (int)K, workspace, stream),
                           "gemv_i8");
@@ -257,6 +240,7 @@ int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uin
     if (rc) return rc;
     if (group != 256 || K % 256) return fail(CONVROT_ERR_GROUP, "%s: W4A4 needs group 256 and K %% 256 == 0", who);
     if (N % 8) return fail(CONVROT_ERR_SHAPE, "%s: N=%lld must be a multiple of 8", who, (long long)N);
+    if (M == 0 || N == 0) return CONVROT_OK;
     if (!wq || !w_scale || !y) return fail(CONVROT_ERR_NULL, "%s: wq, w_scale and y must be non-NULL", who);
     if (!x && (!xq || !x_scale)) return fail(CONVROT_ERR_NULL, "%s: give x, or both xq and x_scale", who);
     if (x && x_dtype != CONVROT_DTYPE_F32 && x_dtype != CONVROT_DTYPE_BF16)
@@ -290,6 +274,7 @@ int convrot_gemm_i4_i32(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t
     int rc = check_shape(M, N, K, 256);
     if (rc) return rc;
     if (K % 256 || N % 8) return fail(CONVROT_ERR_SHAPE, "%s: needs K %% 256 == 0 and N %% 8 == 0", who);
+    if (M == 0 || N == 0) return CONVROT_OK;
     if (!xq || !wq || !acc) return fail(CONVROT_ERR_NULL, "%s: xq, wq and acc must be non-NULL", who);
     if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(acc, 16)) return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
     if (M == 0 || N == 0) return CONVROT_OK;

@@ -9,30 +9,46 @@
 // speed comes from; "INT8 row-scale + ConvRot metadata").
 //
 // Design (MI355X / CDNA4):
-//  * workgroup tile 256(M) x 256(N), 4 wavefronts in 2x2, each owning a 128x128 sub-tile as
-//    4x4 blocks of v_mfma_i32_32x32x32_i8 (256 int32 accumulators per lane);
-//  * K is staged 128 bytes at a time through a double-buffered LDS (2 x 64 KiB) with
-//    buffer_load ... lds (global -> LDS without VGPRs).  Rows are stored with their 16-byte
-//    chunks XOR-swizzled by (row & 7) so the ds_read_b128 fragment reads are conflict-free;
-//    each load instruction still reads whole 128-byte lines.  Out-of-range rows and K chunks
-//    are read through an out-of-bounds buffer offset, which returns zeros;
-//  * blockIdx -> tile mapping gives each of the 8 XCDs a contiguous run of tiles, walked in
-//    groups along M so concurrently running tiles share their weight tile in that XCD's L2;
-//  * the epilogue stages the bf16 tile through LDS (padded rows) and writes Y with fully
-//    coalesced 16-byte stores.
+//  * persistent: one 512-thread workgroup per CU walks a sequence of 256(M) x 256(N) output
+//    tiles; the tiles of each XCD form a contiguous range of the tile order, walked in groups
+//    along M so that the tiles running at the same time share their weight tile in that XCD's
+//    L2.  8 wavefronts (2 per SIMD, so one covers the other's waits) in 2(N) x 4(M) each own a
+//    128x64 sub-tile as 4x2 blocks of v_mfma_i32_32x32x32_i8 (128 int32 accumulators per lane,
+//    in AGPRs, leaving room for a spill-free epilogue);
+//  * K is streamed 64 bytes per K-tile through 4 LDS stages with buffer_load ... lds (global ->
+//    LDS, no VGPRs), 3 K-tiles ahead.  The stream runs across tile boundaries, so the next
+//    tile's first K-tiles load while the current tile finishes and writes its epilogue.
+//    Out-of-range rows read through an out-of-bounds buffer offset, which returns zeros;
+//  * LDS rows are 64 bytes; 16-byte chunk c of row r sits at position c ^ ((r >> 2) & 3).
+//    ds_read_b128 serves 16 lanes (256 bytes, all 64 banks) per cycle and a fragment read puts
+//    16 consecutive rows on them: 4 rows share a 256-byte window and the XOR spreads the 4
+//    windows' rows over distinct positions, so the reads are bank-conflict free;
+//  * one barrier per K-tile, in its middle: by then the next K-tile has landed (it was issued
+//    two K-tiles earlier) and every wave is past its reads of the stage about to be refilled;
+//    fragments are always read one MFMA sub-step ahead;
+//  * the epilogue converts in registers and stores 16 bytes per lane straight to global memory
+//    (lane pairs exchange halves with v_permlane32_swap so each store covers 8 columns); the
+//    tile's sx/sw/bias are loaded into LDS with its first K-tile (4 rotating buffers: with short
+//    K the load side can run up to 3 tiles ahead).
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launchers.hpp"
 
 namespace convrot {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int OPB = 256 * BK;                // bytes of one operand tile per stage (32 KiB)
-constexpr int STAGE = 2 * OPB;               // W tile then X tile
-constexpr int EPI_PITCH = BN * 2 + 16;       // bytes per staged bf16 output row
-constexpr int SMEM = (2 * STAGE > BM * EPI_PITCH) ? 2 * STAGE : BM * EPI_PITCH;
+constexpr int BM = 256, BN = 256, BK = 64, NST = 4;
+constexpr int OPB = 256 * BK;                 // bytes of one operand per stage (16 KiB)
+constexpr int STAGE = 2 * OPB;                // weight rows then token rows
+constexpr int SCALE_OFF = NST * STAGE;        // 128 KiB
+constexpr int SCALE_BYTES = 4 * (2 * BN + BM);
+constexpr int NSCALE = 4;
+constexpr int SMEM = SCALE_OFF + NSCALE * SCALE_BYTES;
+constexpr int NTHREADS = 512;
 constexpr int GROUP_M = 16;
-constexpr uint32_t OOB = 0x80000000u;        // buffer offset past num_records -> loads return 0
+constexpr int WG_PER_CU = 1;
+constexpr uint32_t OOB = 0x80000000u;         // buffer offset past num_records -> loads return 0
 constexpr int NUM_RECORDS = 0x7ffffff0;
 
 struct GemmParams {
@@ -49,12 +65,15 @@ struct GemmParams {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n only.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
 
-__device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int &tm, int &tn)
+// Tile q of the XCD-aware, M-grouped order.  Dispatch ids are spread round-robin over the 8
+// XCDs; virtual id pid (= blockIdx.x + k * gridDim.x, gridDim.x a multiple of 8) keeps its XCD.
+__device__ __forceinline__ void tile_of(int pid, int T, int tiles_m, int tiles_n, int &tm, int &tn)
 {
-    const int T = tiles_m * tiles_n;
     const int xcd = pid & 7, local = pid >> 3;
     const int per = T >> 3, rem = T & 7;
     const int q = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
@@ -66,170 +85,250 @@ __device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int &
     tn = r / gsz;
 }
 
-template <Epi E>
-__global__ void __launch_bounds__(256, 1) gemm_i8_kernel(GemmParams p)
+template <Epi E, bool VEC>
+__global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    const int wn = w & 1, wm = w >> 1;
-    int tm, tn;
-    tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = w & 1, wm = w >> 1;   // wn: 128-row half of N, wm: 64-row quarter of M
     const int K = p.K;
+    const int KT = K / BK;
+    const int T = p.tiles_m * p.tiles_n;
+    // number of tiles of this workgroup: virtual ids blockIdx.x + k*gridDim.x < T
+    const int ntiles = (T - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int total = ntiles * KT;            // K-tiles in this workgroup's stream
 
-    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t *>(p.wq + n0 * K), (short)0, NUM_RECORDS, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t *>(p.xq + m0 * K), (short)0, NUM_RECORDS, 0x00020000);
-
-    // This lane's 16-byte chunk of each of the 8 load instructions per operand and stage:
-    // instruction i of wave w fills LDS rows 8*(4i+w) .. +7; lane -> row +lane/8, swizzled
-    // position lane%8, i.e. K chunk (lane%8) ^ (lane/8).
-    const int lchunk = (lane & 7) ^ (lane >> 3);
-    uint32_t offw[8], offx[8];
-    bool okw[8], okx[8];
+    // Per-lane load geometry (independent of the tile): instruction i (0..1) of wave w fills
+    // LDS rows 16*(8i+w) .. +15 of an operand stage; lane -> row +lane/4 at 16-byte position
+    // lane%4, which holds K chunk (lane%4) ^ swz(row).
+    int lrow[2], lchunk[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = 8 * (4 * i + w) + (lane >> 3);
-        okw[i] = n0 + row < p.N;
-        okx[i] = m0 + row < p.M;
-        offw[i] = (uint32_t)(row * K + 16 * lchunk);
-        offx[i] = offw[i];
+    for (int i = 0; i < 2; ++i) {
+        lrow[i] = 16 * (8 * i + w) + (lane >> 2);
+        lchunk[i] = (lane & 3) ^ swz(lrow[i]);
     }
 
-    auto issue = [&](int kt, int stage) {
-        const int k0 = kt * BK;
-        const bool kok = k0 + 16 * lchunk < K;
-        uint8_t *base = smem + stage * STAGE;
+    // Current load-side tile (the stream runs ahead of the compute-side tile).
+    int ld_t = -1, ld_tm = 0, ld_tn = 0;
+    __amdgpu_buffer_rsrc_t rw, rx;
+    uint32_t offw[2], offx[2];
+    auto set_load_tile = [&](int t) {
+        ld_t = t;
+        tile_of((int)blockIdx.x + t * (int)gridDim.x, T, p.tiles_m, p.tiles_n, ld_tm, ld_tn);
+        const int64_t m0 = (int64_t)ld_tm * BM, n0 = (int64_t)ld_tn * BN;
+        rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(p.wq + n0 * K), (short)0, NUM_RECORDS, 0x00020000);
+        rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(p.xq + m0 * K), (short)0, NUM_RECORDS, 0x00020000);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t ow = (okw[i] && kok) ? offw[i] + k0 : OOB;
-            const uint32_t ox = (okx[i] && kok) ? offx[i] + k0 : OOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + (4 * i + w) * 1024), 16, ow, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(base + OPB + (4 * i + w) * 1024), 16, ox, 0, 0, 0);
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t o = (uint32_t)(lrow[i] * K + 16 * lchunk[i]);
+            offw[i] = n0 + lrow[i] < p.N ? o : OOB;
+            offx[i] = m0 + lrow[i] < p.M ? o : OOB;
+        }
+    };
+    // The tile's sw, bias and sx (256 floats each) go to LDS scale buffer (t & 3) with the
+    // tile's first K-tile: 12 dword load-to-LDS instructions, 2 on each of waves 0-5.
+    // Out-of-range entries and a missing bias read as zeros.
+    auto issue_scales = [&](int t) {
+        if constexpr (E == Epi::Bf16) {
+            const int64_t m0 = (int64_t)ld_tm * BM, n0 = (int64_t)ld_tn * BN;
+            const int64_t nrem = p.N - n0, mrem = p.M - m0;
+            const __amdgpu_buffer_rsrc_t rs[3] = {
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p.sw + n0), (short)0, (int)(4 * (nrem < BN ? nrem : BN)), 0x00020000),
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p.bias ? p.bias + n0 : p.sw), (short)0,
+                                                  p.bias ? (int)(4 * (nrem < BN ? nrem : BN)) : 0, 0x00020000),
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p.sx + m0), (short)0, (int)(4 * (mrem < BM ? mrem : BM)), 0x00020000)};
+            uint8_t *sb = smem + SCALE_OFF + (t & (NSCALE - 1)) * SCALE_BYTES;
+            if (w < 6) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int a = 2 * w + j, arr = a >> 2, part = a & 3;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[arr], (lds_void *)(sb + arr * 1024 + part * 256), 4,
+                                                             (uint32_t)(part * 256 + 4 * lane), 0, 0, 0);
+                }
+            }
+        }
+    };
+    // Issue the loads of the next K-tile of the stream (4 buffer_load ... lds per wave, plus the
+    // scales with a tile's first K-tile) into LDS stage (g & 3).  The load side walks the stream
+    // in order: (ld_t, ld_kt) is the K-tile it issues next.
+    int ld_kt = 0;
+    auto issue = [&](int g) {
+        if (ld_kt == 0) {
+            set_load_tile(ld_t + 1);
+            issue_scales(ld_t);
+        }
+        const uint32_t k0 = (uint32_t)(ld_kt * BK);
+        if (++ld_kt == KT) ld_kt = 0;
+        uint8_t *base = smem + (g & (NST - 1)) * STAGE + w * 1024;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + 8 * i * 1024), 16,
+                                                     offw[i] == OOB ? OOB : offw[i] + k0, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(base + OPB + 8 * i * 1024), 16,
+                                                     offx[i] == OOB ? OOB : offx[i] + k0, 0, 0, 0);
         }
     };
 
-    v16i acc[4][4];
+    // Fragment addressing: row = wave base + 32*blk + lane%32 (bases are multiples of 32, so
+    // swz(row) == swz(lane%32)); sub-step kk reads K chunk 2*kk + lane/32.
+    const int frow = lane & 31, fhalf = lane >> 5;
+    const int arow = (wn * 128 + frow) * BK, brow = OPB + (wm * 64 + frow) * BK;
+    const int fpos[2] = {((0 + fhalf) ^ swz(frow)) * 16, ((2 + fhalf) ^ swz(frow)) * 16};
+    v4i fa[2][4], fb[2][2];
+    auto read_frags = [&](int g, int kk, int buf) {
+        const uint8_t *s0 = smem + (g & (NST - 1)) * STAGE + fpos[kk];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) fa[buf][b] = *reinterpret_cast<const v4i *>(s0 + arow + 32 * b * BK);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) fb[buf][b] = *reinterpret_cast<const v4i *>(s0 + brow + 32 * b * BK);
+    };
+    v16i acc[4][2];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = v16i{};
-
-    // Fragment addressing: row = wave base + 32*blk + lane%32 (so row & 7 == lane & 7) and
-    // K chunk = 2*kk + lane/32 of the 8 chunks of a 128-byte stage row.
-    const int frow = lane & 31, fhalf = lane >> 5, fsw = lane & 7;
-    const int arow = (wn * 128 + frow) * BK, brow = OPB + (wm * 128 + frow) * BK;
-    v4i fa[2][4], fb[2][4];
-    auto read_frags = [&](int stage, int kk, int buf) {
-        const uint8_t *s0 = smem + stage * STAGE;
-        const int pos = ((2 * kk + fhalf) ^ fsw) * 16;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            fa[buf][b] = *reinterpret_cast<const v4i *>(s0 + arow + 32 * b * BK + pos);
-            fb[buf][b] = *reinterpret_cast<const v4i *>(s0 + brow + 32 * b * BK + pos);
-        }
-    };
+        for (int b = 0; b < 2; ++b) acc[a][b] = v16i{};
     auto mfmas = [&](int buf) {
 #pragma unroll
-        for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-            for (int bj = 0; bj < 4; ++bj)
-                acc[bi][bj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[buf][bi], fb[buf][bj], acc[bi][bj], 0, 0, 0);
-    };
-
-    // Pipeline: LDS holds tiles t (being read) and t+1 (landing).  Each tile's last fragments
-    // are read into registers before the barrier, so right after it the stage of tile t is
-    // refilled with tile t+2 and tile t+1's first fragments are read while the last 16 MFMAs
-    // of tile t run.
-    const int KT = (K + BK - 1) / BK;
-    issue(0, 0);
-    if (KT > 1) {
-        issue(1, 1);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));   // tile 0 landed, tile 1 in flight
-    } else {
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    }
-    __syncthreads();
-    read_frags(0, 0, 0);
-
-    for (int kt = 0; kt < KT; ++kt) {
-        const int stage = kt & 1;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            if (kk < 3) {
-                read_frags(stage, kk + 1, (kk + 1) & 1);
-            } else {
-                __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): tile t+1 landed, tile t read
-                __syncthreads();
-                if (kt + 2 < KT) issue(kt + 2, stage);
-                if (kt + 1 < KT) read_frags(stage ^ 1, 0, 0);
-            }
-            mfmas(kk & 1);
+        for (int j = 0; j < 8; ++j) {
+            const int bi = j >> 1, bj = j & 1;
+            acc[bi][bj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[buf][bi], fb[buf][bj], acc[bi][bj], 0, 0, 0);
         }
-    }
+    };
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
     // Accumulator layout of a 32x32 block (MFMA rows = weight rows n, columns = tokens m):
     // lane holds m = lane%32 and, for register v, n = 8*(v/4) + 4*(lane/32) + v%4.
-    if constexpr (E == Epi::Int32) {
-        int32_t *y = static_cast<int32_t *>(p.y);
+    // Stores go through a buffer descriptor per 32-row block (uniform, in SGPRs) with 32-bit
+    // lane offsets; out-of-range rows/columns get an out-of-bounds offset and are dropped.  This
+    // keeps the epilogue's register footprint small: a spill reload here would wait on vmcnt
+    // and so drain every store and prefetch in flight.
+    auto epilogue = [&](int t) {
+        int tm, tn;
+        tile_of((int)blockIdx.x + t * (int)gridDim.x, T, p.tiles_m, p.tiles_n, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        const int Mi = (int)p.M, Ni = (int)p.N;
+        // lane-dependent bases laundered so the addresses below are formed here, not hoisted out
+        // of the tile loop (where they would stay live through the main loop)
+        int erow = frow, ecol = wn * 128 + 4 * fhalf;
+        asm volatile("" : "+v"(erow), "+v"(ecol));
+        if constexpr (E == Epi::Int32) {
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-            const int64_t m = m0 + wm * 128 + 32 * bj + frow;
-            if (m >= p.M) continue;
+            for (int bj = 0; bj < 2; ++bj) {
+                const int mr = m0 + wm * 64 + 32 * bj;            // first row of the block (uniform)
+                const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+                    static_cast<int32_t *>(p.y) + (int64_t)mr * p.N, (short)0, NUM_RECORDS, 0x00020000);
+                const bool rok = mr + erow < Mi;
 #pragma unroll
-            for (int bi = 0; bi < 4; ++bi)
+                for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-                for (int g = 0; g < 4; ++g)
+                    for (int g = 0; g < 4; ++g) {
+                        const int n = n0 + ecol + 32 * bi + 8 * g;
+                        const v4u d = {(unsigned)acc[bi][bj][4 * g], (unsigned)acc[bi][bj][4 * g + 1],
+                                       (unsigned)acc[bi][bj][4 * g + 2], (unsigned)acc[bi][bj][4 * g + 3]};
+                        if (VEC || n + 3 < Ni) {
+                            const uint32_t off = (rok && n < Ni) ? (uint32_t)(erow * Ni + n) * 4u : OOB;
+                            __builtin_amdgcn_raw_buffer_store_b128(d, ry, off, 0, 0);
+                        } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int64_t n = n0 + wn * 128 + 32 * bi + 8 * g + 4 * fhalf + i;
-                        if (n < p.N) y[m * p.N + n] = acc[bi][bj][4 * g + i];
+                            for (int e = 0; e < 4; ++e) {
+                                const uint32_t off = (rok && n + e < Ni) ? (uint32_t)(erow * Ni + n + e) * 4u : OOB;
+                                __builtin_amdgcn_raw_buffer_store_b32(d[e], ry, off, 0, 0);
+                            }
+                        }
                     }
-        }
-    } else {
+                fence();
+            }
+        } else {
+            const float *ls = reinterpret_cast<const float *>(smem + SCALE_OFF + (t & (NSCALE - 1)) * SCALE_BYTES);
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-            const int ml = wm * 128 + 32 * bj + frow;
-            const int64_t m = m0 + ml;
-            const float sxm = m < p.M ? p.sx[m] : 0.0f;
+            for (int bj = 0; bj < 2; ++bj) {
+                const int mr = m0 + wm * 64 + 32 * bj;
+                const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+                    static_cast<uint16_t *>(p.y) + (int64_t)mr * p.N, (short)0, NUM_RECORDS, 0x00020000);
+                const bool rok = mr + erow < Mi;
+                const float sxm = ls[2 * BN + wm * 64 + 32 * bj + erow];
 #pragma unroll
-            for (int bi = 0; bi < 4; ++bi)
+                for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int nl = wn * 128 + 32 * bi + 8 * g + 4 * fhalf;
-                    float yv[4];
+                    for (int g2 = 0; g2 < 2; ++g2) {
+                        // column groups g = 2*g2 and 2*g2+1 of block bi: 4 columns each per lane
+                        uint32_t pk[2][2];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int64_t n = n0 + nl + i;
-                        const float swn = n < p.N ? p.sw[n] : 0.0f;
-                        const float bn = (p.bias && n < p.N) ? p.bias[n] : 0.0f;
-                        yv[i] = __builtin_fmaf((float)acc[bi][bj][4 * g + i], sxm * swn, bn);
+                        for (int h = 0; h < 2; ++h) {
+                            const int g = 2 * g2 + h;
+                            const int nl = ecol + 32 * bi + 8 * g;
+                            const v4f s4 = *reinterpret_cast<const v4f *>(ls + nl);
+                            const v4f b4 = *reinterpret_cast<const v4f *>(ls + BN + nl);
+                            float yv[4];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                yv[i] = __builtin_fmaf((float)acc[bi][bj][4 * g + i], sxm * s4[i], b4[i]);
+                            pk[h][0] = pack_bf16x2(yv[0], yv[1]);
+                            pk[h][1] = pack_bf16x2(yv[2], yv[3]);
+                        }
+                        // lane l < 32 now gets columns 8g..8g+7 of group g = 2*g2, lane l+32 those
+                        // of group 2*g2+1 (same token row m)
+                        swap32(pk[0][0], pk[1][0]);
+                        swap32(pk[0][1], pk[1][1]);
+                        const int n = n0 + (ecol - 4 * fhalf) + 32 * bi + 8 * (2 * g2 + fhalf);
+                        if constexpr (VEC) {
+                            const uint32_t off = (rok && n < Ni) ? (uint32_t)(erow * Ni + n) * 2u : OOB;
+                            __builtin_amdgcn_raw_buffer_store_b128(v4u{pk[0][0], pk[0][1], pk[1][0], pk[1][1]}, ry, off, 0, 0);
+                        } else {
+                            // rows not 16-byte aligned (N % 8 != 0): element stores, clipped at N
+                            const uint32_t wv[4] = {pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const uint32_t off = (rok && n + e < Ni) ? (uint32_t)(erow * Ni + n + e) * 2u : OOB;
+                                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(wv[e >> 1] >> (16 * (e & 1))), ry, off, 0, 0);
+                            }
+                        }
                     }
-                    uint2 pk;
-                    pk.x = pack_bf16x2(yv[0], yv[1]);
-                    pk.y = pack_bf16x2(yv[2], yv[3]);
-                    *reinterpret_cast<uint2 *>(smem + ml * EPI_PITCH + nl * 2) = pk;
-                }
-        }
-        __syncthreads();
-        uint16_t *y = static_cast<uint16_t *>(p.y);
-        const int ch = threadIdx.x & 31;
-        const bool vec = (p.N & 7) == 0;
-        for (int rp = 0; rp < BM; rp += 8) {
-            const int row = rp + (threadIdx.x >> 5);
-            const int64_t m = m0 + row;
-            const int64_t n = n0 + 8 * ch;
-            if (m >= p.M || n >= p.N) continue;
-            const uint4 v = *reinterpret_cast<const uint4 *>(smem + row * EPI_PITCH + 16 * ch);
-            if (vec) {
-                *reinterpret_cast<uint4 *>(y + m * p.N + n) = v;
-            } else {
-                const uint16_t *e = reinterpret_cast<const uint16_t *>(&v);
-                for (int i = 0; i < 8 && n + i < p.N; ++i) y[m * p.N + n + i] = e[i];
+                fence();
             }
         }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) acc[a][b] = v16i{};
+    };
+
+    if (ntiles <= 0) return;
+    // prologue: K-tiles 0..2 in flight, K-tile 0 (and tile 0's scales) visible, first fragments
+    issue(0);
+    if (total > 1) issue(1);
+    if (total > 2) issue(2);
+    if (total > 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+    else if (total > 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    read_frags(0, 0, 0);
+
+    int g = 0;
+    for (int t = 0; t < ntiles; ++t) {
+        for (int kt = 0; kt < KT; ++kt, ++g) {
+            read_frags(g, 1, 1);
+            fence();
+            mfmas(0);
+            fence();
+            // K-tile g+1 must have landed.  Issued after its loads: K-tile g+2's 4 loads and, in
+            // the first two K-tiles of a tile, the previous tile's 16 epilogue stores (vmcnt
+            // counts stores too; they may keep draining).
+            if (g + 2 < total) {
+                if (t > 0 && kt < 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(20));
+                else __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+            } else {
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            }
+            __syncthreads();
+            if (g + 3 < total) issue(g + 3);
+            if (g + 1 < total) read_frags(g + 1, 0, 0);
+            fence();
+            mfmas(1);
+            fence();
+        }
+        epilogue(t);
     }
 }
 
@@ -239,6 +338,12 @@ hipError_t launch_gemm_i8(const int8_t *xq, const int8_t *wq, const float *sx, c
                           void *y, Epi epi, int64_t M, int64_t N, int K, hipStream_t stream)
 {
     if (M <= 0 || N <= 0) return hipSuccess;
+    static int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            n = 256;
+        return n > 0 ? n : 256;
+    }();
     GemmParams p;
     p.xq = xq;
     p.wq = wq;
@@ -251,11 +356,16 @@ hipError_t launch_gemm_i8(const int8_t *xq, const int8_t *wq, const float *sx, c
     p.K = K;
     p.tiles_m = (int)((M + BM - 1) / BM);
     p.tiles_n = (int)((N + BN - 1) / BN);
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(256);
+    const int T = p.tiles_m * p.tiles_n;
+    // persistent grid: a multiple of 8 (XCD count) so virtual ids keep their XCD
+    int grid = cus * WG_PER_CU;
+    if (T < grid) grid = (T + 7) & ~7;
     if (epi == Epi::Int32)
-        hipLaunchKernelGGL(gemm_i8_kernel<Epi::Int32>, grid, block, 0, stream, p);
+        hipLaunchKernelGGL((gemm_i8_kernel<Epi::Int32, true>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
+    else if (N % 8 == 0)
+        hipLaunchKernelGGL((gemm_i8_kernel<Epi::Bf16, true>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
     else
-        hipLaunchKernelGGL(gemm_i8_kernel<Epi::Bf16>, grid, block, 0, stream, p);
+        hipLaunchKernelGGL((gemm_i8_kernel<Epi::Bf16, false>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -19,9 +19,10 @@ enum class Epi { Bf16 = 0, Int32 = 1 };
 hipError_t launch_gemm_i8(const int8_t *xq, const int8_t *wq, const float *sx, const float *sw, const float *bias,
                           void *y, Epi epi, int64_t M, int64_t N, int K, hipStream_t stream);
 
-// Same contraction for M <= 16 (weight streaming, split-K).  `ws` holds M*N int32 partial sums
-// followed by ceil(N/64) counters and must be zero on entry (gemv_i8_workspace_bytes bytes).
-size_t gemv_i8_workspace_bytes(int64_t M, int64_t N);
+// Same contraction for M <= 16 (weight streaming, split-K).  `ws` is scratch of
+// gemv_i8_workspace_bytes() bytes (0 when K is not split); its contents on entry do not matter.
+int gemv_i8_splits(int64_t N, int K);
+size_t gemv_i8_workspace_bytes(int64_t M, int64_t N, int K);
 hipError_t launch_gemv_i8(const int8_t *xq, const int8_t *wq, const float *sx, const float *sw, const float *bias,
                           void *y, Epi epi, int64_t M, int64_t N, int K, void *ws, hipStream_t stream);
 

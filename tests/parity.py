@@ -30,14 +30,26 @@ def to_np64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def check_codes(gpu: np.ndarray, ref: np.ndarray, what: str = "codes", rate: float = CODE_MISMATCH_RATE):
+def allowed_mismatches(n: int, rate: float) -> float:
+    """Mismatch count compatible with `rate` on a sample of n codes: the expectation plus a
+    3-sigma Poisson margin and 2 events, so a small sample is not failed by one or two edge
+    cases (exact half-integer quotients do occur with bf16 inputs) while large samples are held
+    to the rate itself."""
+    lam = rate * n
+    return lam + 3.0 * np.sqrt(lam) + 2.0
+
+
+def check_codes(gpu: np.ndarray, ref: np.ndarray, what: str = "codes", rate: float = CODE_MISMATCH_RATE,
+                slack: bool = True):
     gpu = gpu.astype(np.int64)
     ref = ref.astype(np.int64)
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
     d = np.abs(gpu - ref)
     mism = np.count_nonzero(d)
     assert d.max(initial=0) <= 1, "%s: max |delta| = %d" % (what, d.max())
-    assert mism <= rate * d.size, "%s: %d mismatches of %d (rate %.2e)" % (what, mism, d.size, mism / max(d.size, 1))
+    limit = allowed_mismatches(d.size, rate) if slack else rate * d.size
+    assert mism <= limit, "%s: %d mismatches of %d (rate %.2e, limit %.1f)" % (
+        what, mism, d.size, mism / max(d.size, 1), limit)
     return mism
 
 

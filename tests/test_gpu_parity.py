@@ -62,6 +62,18 @@ def test_quantize_int8_parity(cr, rows, K, g, dtype):
     P.check_codes(_np(q), qr)
 
 
+@pytest.mark.parametrize("g", [1, 256])
+def test_quantize_code_mismatch_rate_large_sample(cr, g):
+    """Rule (a) held to the rate itself (no small-sample allowance) on 2M codes."""
+    x, _, _ = workloads.ragged_case(512, 4096, 8, seed=77 + g)
+    q, s = cr.quantize_act(x.to(DEV), group=g, bits=8)
+    torch.cuda.synchronize()
+    qr, sr = orc.quantize_act_i8(_x64(x), g)
+    P.check_scales_f32(_np(s), sr)
+    n = P.check_codes(_np(q), qr, slack=False)
+    P.say("g=%d: %d mismatches in %d codes" % (g, n, qr.size))
+
+
 def test_quantize_zero_rows_and_single_outlier(cr):
     x = torch.zeros(6, 512)
     x[1, 7] = 1000.0
