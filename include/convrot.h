@@ -110,6 +110,7 @@ int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_
  *   xq uint8 [M, K/2] / x_scale fp16 [K/256, M] from convrot_quantize_act(bits = 4).
  *   wq uint8 [N, K/2], w_scale fp16 [K/256, N] from convrot_prepare_weight(bits = 4).
  *   group must be 256, K % 256 == 0, N % 8 == 0.  bias fp32 [N] or NULL; y bf16 [M, N].
+ *   w_scale must be 8-byte aligned (the kernel reads 4 scales at a time).
  */
 int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uint16_t *x_scale, int64_t M,
                         int64_t N, int64_t K, int group, const uint8_t *wq, const uint16_t *w_scale,

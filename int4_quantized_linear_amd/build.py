@@ -43,7 +43,9 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
         list(ex.map(_compile, SOURCES, objs))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [_hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs]
+    # the version script keeps the internal C++ launchers local: only convrot_* is exported
+    cmd = [_hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH,
+           "-Wl,--version-script=" + os.path.join(CSRC, "libconvrot.map"), "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))

@@ -36,14 +36,16 @@ int log2i(int g)
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-int check_shape(int64_t M, int64_t N, int64_t K, int group)
+int check_shape(int64_t M, int64_t N, int64_t K, int group, const char *who)
 {
     if (M < 0 || N < 0 || M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
-        return fail(CONVROT_ERR_SHAPE, "M=%lld N=%lld must be in [0, 2^31)", (long long)M, (long long)N);
+        return fail(CONVROT_ERR_SHAPE, "%s: M=%lld N=%lld must be in [0, 2^31)", who, (long long)M, (long long)N);
     if (K < 64 || K > CONVROT_MAX_K || K % 64)
-        return fail(CONVROT_ERR_SHAPE, "K=%lld must be a multiple of 64 in [64, %d]", (long long)K, CONVROT_MAX_K);
-    if (!pow2_group(group)) return fail(CONVROT_ERR_GROUP, "group=%d must be a power of two in [1, 256]", group);
-    if (K % group) return fail(CONVROT_ERR_SHAPE, "K=%lld is not a multiple of group=%d", (long long)K, group);
+        return fail(CONVROT_ERR_SHAPE, "%s: K=%lld must be a multiple of 64 in [64, %d]", who, (long long)K,
+                    CONVROT_MAX_K);
+    if (!pow2_group(group))
+        return fail(CONVROT_ERR_GROUP, "%s: group=%d must be a power of two in [1, 256]", who, group);
+    if (K % group) return fail(CONVROT_ERR_SHAPE, "%s: K=%lld is not a multiple of group=%d", who, (long long)K, group);
     return CONVROT_OK;
 }
 
@@ -112,7 +114,7 @@ int quantize_common(const void *x, int dtype, int64_t R, int64_t K, int group, i
     if (!x || !q || !scale) return fail(CONVROT_ERR_NULL, "%s: x, q and scale must be non-NULL", who);
     if (dtype != CONVROT_DTYPE_F32 && dtype != CONVROT_DTYPE_BF16) return fail(CONVROT_ERR_DTYPE, "%s: dtype=%d", who, dtype);
     if (bits != 8 && bits != 4) return fail(CONVROT_ERR_BITS, "%s: bits=%d", who, bits);
-    int rc = check_shape(R, 1, K, group);
+    int rc = check_shape(R, 1, K, group, who);
     if (rc) return rc;
     if (bits == 4 && (group != 256 || K % 256))
         return fail(CONVROT_ERR_GROUP, "%s: INT4 needs group 256 and K %% 256 == 0 (group=%d, K=%lld)", who, group, (long long)K);
@@ -171,7 +173,7 @@ int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_
                    void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     const char *who = "convrot_linear";
-    int rc = check_shape(M, N, K, group);
+    int rc = check_shape(M, N, K, group, who);
     if (rc) return rc;
     if (M == 0 || N == 0) return CONVROT_OK;
     if (!wq || !w_scale || !y) return fail(CONVROT_ERR_NULL, "%s: wq, w_scale and y must be non-NULL", who);
@@ -211,7 +213,7 @@ int convrot_gemm_i8_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N
                         void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     const char *who = "convrot_gemm_i8_i32";
-    int rc = check_shape(M, N, K, 1);
+    int rc = check_shape(M, N, K, 1, who);
     if (rc) return rc;
     if (M == 0 || N == 0) return CONVROT_OK;
     if (!xq || !wq || !acc) return fail(CONVROT_ERR_NULL, "%s: xq, wq and acc must be non-NULL", who);
@@ -236,7 +238,7 @@ int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uin
                         const float *bias, void *y, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     const char *who = "convrot_linear_w4a4";
-    int rc = check_shape(M, N, K, group);
+    int rc = check_shape(M, N, K, group, who);
     if (rc) return rc;
     if (group != 256 || K % 256) return fail(CONVROT_ERR_GROUP, "%s: W4A4 needs group 256 and K %% 256 == 0", who);
     if (N % 8) return fail(CONVROT_ERR_SHAPE, "%s: N=%lld must be a multiple of 8", who, (long long)N);
@@ -271,7 +273,7 @@ int convrot_gemm_i4_i32(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t
                         hipStream_t stream)
 {
     const char *who = "convrot_gemm_i4_i32";
-    int rc = check_shape(M, N, K, 256);
+    int rc = check_shape(M, N, K, 256, who);
     if (rc) return rc;
     if (K % 256 || N % 8) return fail(CONVROT_ERR_SHAPE, "%s: needs K %% 256 == 0 and N %% 8 == 0", who);
     if (M == 0 || N == 0) return CONVROT_OK;

@@ -1,0 +1,177 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no kernel launched).
+
+* every function declared in include/convrot.h is exported by libconvrot.so and has a ctypes
+  signature in the binding;
+* status names and the workspace-size query;
+* every precondition violation returns its status code (and a message) before anything touches
+  the device: the arguments below always break a rule the library checks first, and pointers are
+  fake but never dereferenced because the call is rejected on the host.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convrot.h")
+
+cr = pytest.importorskip("int4_quantized_linear_amd.convrot")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(convrot_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(cr.LIB_PATH):
+        pytest.fail("libconvrot.so is not built; run python -m int4_quantized_linear_amd.build")
+    return cr.load()
+
+
+def test_header_declares_the_boundary():
+    fns = header_functions()
+    for name in ("convrot_prepare_weight", "convrot_quantize_act", "convrot_linear", "convrot_linear_w4a4",
+                 "convrot_workspace_bytes", "convrot_gemm_i8_i32", "convrot_gemm_i4_i32", "convrot_last_error",
+                 "convrot_status_string"):
+        assert name in fns
+    assert set(fns) == set(cr.SIGNATURES), "binding signatures and header disagree"
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", cr.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in header_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_exports_are_c_linkage_only(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", cr.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    ours = sorted({ln.split()[-1] for ln in out.splitlines() if " T " in ln and "convrot" in ln})
+    assert ours == header_functions(), ours
+
+
+def test_status_strings(lib):
+    for code, name in cr.STATUS.items():
+        assert lib.convrot_status_string(code).decode() == name
+    assert lib.convrot_status_string(99).decode() == "CONVROT_ERR_UNKNOWN"
+
+
+def test_workspace_bytes(lib):
+    ws = lib.convrot_workspace_bytes
+    assert ws(-1, 8, 256, 8) == 0 and ws(4, -1, 256, 8) == 0 and ws(4, 8, 0, 8) == 0 and ws(4, 8, 256, 5) == 0
+    for M, N, K in [(4096, 16128, 5376), (17, 256, 512), (12, 8192, 5120), (12, 5120, 25600), (1, 64, 64)]:
+        b8 = ws(M, N, K, 8)
+        assert b8 % 256 == 0 and b8 >= M * K + 4 * M, (M, N, K)
+    for M, K in [(4096, 5376), (3, 512)]:
+        b4 = ws(M, 1024, K, 4)
+        assert b4 % 256 == 0 and b4 >= M * K // 2 + 2 * M * (K // 256)
+
+
+A = 0x100000          # fake 256-byte aligned device addresses (never dereferenced)
+B = 0x200000
+C = 0x300000
+D = 0x400000
+E = 0x500000
+MIS = 0x100002        # misaligned
+
+
+def q_args(x=A, dtype=1, R=4, K=512, group=256, bits=8, q=B, s=C):
+    return (x, dtype, R, K, group, bits, q, s, None)
+
+
+def lin_args(x=A, dt=1, xq=None, xs=None, M=32, N=256, K=512, group=256, wq=B, sw=C, bias=None, y=D, ws=E,
+             wsb=1 << 30):
+    return (x, dt, xq, xs, M, N, K, group, wq, sw, bias, y, ws, wsb, None)
+
+
+def w4_args(x=A, dt=1, xq=None, xs=None, M=32, N=256, K=512, group=256, wq=B, sw=C, bias=None, y=D, ws=E,
+            wsb=1 << 30):
+    return (x, dt, xq, xs, M, N, K, group, wq, sw, bias, y, ws, wsb, None)
+
+
+ERR = {name: code for code, name in cr.STATUS.items()}
+CASES = [
+    # quantize / prepare
+    ("convrot_quantize_act", q_args(x=None), "CONVROT_ERR_NULL"),
+    ("convrot_quantize_act", q_args(s=None), "CONVROT_ERR_NULL"),
+    ("convrot_quantize_act", q_args(dtype=7), "CONVROT_ERR_DTYPE"),
+    ("convrot_quantize_act", q_args(bits=6), "CONVROT_ERR_BITS"),
+    ("convrot_quantize_act", q_args(K=500), "CONVROT_ERR_SHAPE"),
+    ("convrot_quantize_act", q_args(K=0), "CONVROT_ERR_SHAPE"),
+    ("convrot_quantize_act", q_args(K=131072 + 64), "CONVROT_ERR_SHAPE"),
+    ("convrot_quantize_act", q_args(R=-1), "CONVROT_ERR_SHAPE"),
+    ("convrot_quantize_act", q_args(R=1 << 31), "CONVROT_ERR_SHAPE"),
+    ("convrot_quantize_act", q_args(group=3), "CONVROT_ERR_GROUP"),
+    ("convrot_quantize_act", q_args(group=512), "CONVROT_ERR_GROUP"),
+    ("convrot_quantize_act", q_args(K=192, group=128), "CONVROT_ERR_SHAPE"),
+    ("convrot_quantize_act", q_args(bits=4, group=128), "CONVROT_ERR_GROUP"),
+    ("convrot_quantize_act", q_args(bits=4, K=320, group=64), "CONVROT_ERR_GROUP"),
+    ("convrot_quantize_act", q_args(x=MIS), "CONVROT_ERR_ALIGN"),
+    ("convrot_quantize_act", q_args(q=MIS), "CONVROT_ERR_ALIGN"),
+    ("convrot_quantize_act", q_args(s=C + 2), "CONVROT_ERR_ALIGN"),
+    ("convrot_prepare_weight", q_args(q=None), "CONVROT_ERR_NULL"),
+    ("convrot_prepare_weight", q_args(dtype=2), "CONVROT_ERR_DTYPE"),
+    ("convrot_prepare_weight", q_args(group=0), "CONVROT_ERR_GROUP"),
+    # INT8 linear
+    ("convrot_linear", lin_args(K=100), "CONVROT_ERR_SHAPE"),
+    ("convrot_linear", lin_args(group=100), "CONVROT_ERR_GROUP"),
+    ("convrot_linear", lin_args(wq=None), "CONVROT_ERR_NULL"),
+    ("convrot_linear", lin_args(y=None), "CONVROT_ERR_NULL"),
+    ("convrot_linear", lin_args(x=None, xq=A), "CONVROT_ERR_NULL"),
+    ("convrot_linear", lin_args(dt=5), "CONVROT_ERR_DTYPE"),
+    ("convrot_linear", lin_args(y=MIS), "CONVROT_ERR_ALIGN"),
+    ("convrot_linear", lin_args(bias=E + 1), "CONVROT_ERR_ALIGN"),
+    ("convrot_linear", lin_args(x=None, xq=A, xs=C + 2), "CONVROT_ERR_ALIGN"),
+    ("convrot_linear", lin_args(ws=None), "CONVROT_ERR_WORKSPACE"),
+    ("convrot_linear", lin_args(wsb=16), "CONVROT_ERR_WORKSPACE"),
+    ("convrot_linear", lin_args(ws=E + 16), "CONVROT_ERR_WORKSPACE"),
+    ("convrot_linear", lin_args(x=None, xq=A, xs=C, M=12, N=8192, K=5120, ws=None, wsb=0), "CONVROT_ERR_WORKSPACE"),
+    # W4A4 linear
+    ("convrot_linear_w4a4", w4_args(group=128), "CONVROT_ERR_GROUP"),
+    ("convrot_linear_w4a4", w4_args(K=320, group=64), "CONVROT_ERR_GROUP"),
+    ("convrot_linear_w4a4", w4_args(N=252), "CONVROT_ERR_SHAPE"),
+    ("convrot_linear_w4a4", w4_args(sw=None), "CONVROT_ERR_NULL"),
+    ("convrot_linear_w4a4", w4_args(x=None, xs=C), "CONVROT_ERR_NULL"),
+    ("convrot_linear_w4a4", w4_args(dt=9), "CONVROT_ERR_DTYPE"),
+    ("convrot_linear_w4a4", w4_args(sw=C + 2), "CONVROT_ERR_ALIGN"),
+    ("convrot_linear_w4a4", w4_args(ws=None), "CONVROT_ERR_WORKSPACE"),
+    # integer cores
+    ("convrot_gemm_i8_i32", (A, B, 32, 256, 96, C, None, 0, None), "CONVROT_ERR_SHAPE"),
+    ("convrot_gemm_i8_i32", (None, B, 32, 256, 512, C, None, 0, None), "CONVROT_ERR_NULL"),
+    ("convrot_gemm_i8_i32", (A, B, 32, 256, 512, MIS, None, 0, None), "CONVROT_ERR_ALIGN"),
+    ("convrot_gemm_i8_i32", (A, B, 12, 256, 8192, C, None, 0, None), "CONVROT_ERR_WORKSPACE"),
+    ("convrot_gemm_i4_i32", (A, B, 32, 256, 320, C, None), "CONVROT_ERR_SHAPE"),
+    ("convrot_gemm_i4_i32", (A, B, 32, 250, 512, C, None), "CONVROT_ERR_SHAPE"),
+    ("convrot_gemm_i4_i32", (A, None, 32, 256, 512, C, None), "CONVROT_ERR_NULL"),
+    ("convrot_gemm_i4_i32", (A, B + 4, 32, 256, 512, C, None), "CONVROT_ERR_ALIGN"),
+]
+
+
+@pytest.mark.parametrize("name,args,status", CASES, ids=["%s-%d-%s" % (c[0][8:], i, c[2][12:]) for i, c in enumerate(CASES)])
+def test_precondition_errors(lib, name, args, status):
+    rc = getattr(lib, name)(*args)
+    assert rc == ERR[status], (cr.STATUS.get(rc, rc), lib.convrot_last_error().decode())
+    assert name in lib.convrot_last_error().decode()
+
+
+def test_empty_inputs_are_noops(lib):
+    # M == 0 or N == 0: OK without any pointer and without touching a device
+    assert lib.convrot_quantize_act(None, 1, 0, 512, 256, 8, None, None, None) == 0
+    assert lib.convrot_linear(None, 1, None, None, 0, 256, 512, 256, None, None, None, None, None, 0, None) == 0
+    assert lib.convrot_linear(None, 1, None, None, 16, 0, 512, 256, None, None, None, None, None, 0, None) == 0
+    assert lib.convrot_linear_w4a4(None, 1, None, None, 0, 256, 512, 256, None, None, None, None, None, 0, None) == 0
+    assert lib.convrot_gemm_i8_i32(None, None, 0, 256, 512, None, None, 0, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    # the Python layer never falls back to another implementation
+    monkeypatch.setattr(cr, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(cr, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        cr.load()
