@@ -3,23 +3,31 @@
 
 One step = one ConvRot INT8 linear at the prefill workload (M=4096 tokens, K=5376, N=16128,
 bf16 activations with outlier channels, prepared INT8 weights, fp32 bias, bf16 out):
-rotate+quantize the activations (KR1), then the INT8 MFMA GEMM with the fused dequant epilogue
-(KR2).  Inputs and weights cycle through rings of distinct buffers (>= 1 GiB each) so every
-step reads HBM rather than the 256 MB last-level cache.  `value` is whole-step int8 TOP/s.
+rotate+quantize the activations, then the INT8 MFMA GEMM with the fused dequant epilogue.
+Inputs and weights cycle through rings of distinct buffers (>= 1 GiB each), so every step
+reads HBM rather than the last-level cache.  `value` is whole-step int8 TOP/s.
 
-The same run also measures, with its own timed loops of the same length:
+The same run also measures, each with its own timed loop:
   * decode (M=12) linears on the four Qwen3-VL-32B-like shapes: weight GB/s of the split-K
-    GEMV kernel (x pre-quantized) and end-to-end (rotate+quantize + GEMV);
-  * the W4A4 linear at M=4096, K=5376, N=10752 and the 20% W8A8 mixed profile;
+    GEMV (x pre-quantized) and end to end (rotate+quantize + GEMV), replayed from HIP graphs
+    so that host launch gaps are not counted (eager times are reported beside them);
+  * the W4A4 linear at M=4096, K=5376, N=10752 and the mixed profile with 20% W8A8 layers;
+  * the 64-layer Qwen3-32B-shaped stack at M=2048 (all weights resident, 31 GB of INT8);
   * the CPU oracle on a bounded sample of the prefill workload (cpu_baseline).
 Per-kernel durations come from HIP events recorded on the stream the kernels run on.
+
+Counter runs (HBM traffic): `--only copy` runs a plain 256 MiB device copy for calibrating
+FETCH_SIZE / WRITE_SIZE; `--pmc-summary` turns four rocprofv3 counter CSVs into
+profiles/hbm_traffic.json, which this script reads back for the roofline's `traffic`.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -29,6 +37,10 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s (published)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s (published)
 RING_BYTES = 1 << 30
+COPY_PROBE_BYTES = 256 << 20
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = {"gemm_i8": "gemm_i8.hip", "rotate_quant": "rotate_quant.hip", "gemv_i8": "gemv_i8.hip",
+                  "gemm_w4a4": "gemm_w4a4.hip"}
 
 
 def log(*a):
@@ -41,13 +53,40 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a4"], default="all",
-                    help="restrict the measured workloads (profiling runs)")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a4", "stack", "copy"], default="all",
+                    help="restrict the measured workloads (profiling runs); 'copy' = the counter calibration copy")
+    ap.add_argument("--stack-layers", type=int, default=64)
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/hbm_traffic.json from rocprofv3 --pmc counter CSVs and exit")
     return ap.parse_args()
 
 
 def ring_count(bytes_each: int) -> int:
     return max(2, -(-RING_BYTES // max(bytes_each, 1)))
+
+
+def src_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "int4_quantized_linear_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(key: str, current_hash: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the current
+    kernel source; otherwise None."""
+    try:
+        d = json.load(open(TRAFFIC_JSON))["kernels"].get(key)
+    except (OSError, ValueError, KeyError):
+        return None
+    if not d or d.get("source_hash") != current_hash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------------------------------------
+# timing helpers
 
 
 def timed_loop(fn, steps: int, warmup: int, torch):
@@ -64,31 +103,36 @@ def timed_loop(fn, steps: int, warmup: int, torch):
     return wall, marks
 
 
-def ev_ms(a, b):
-    return a.elapsed_time(b)
+def graph_time_us(torch, launch, n_calls: int, reps: int) -> float:
+    """Capture n_calls launches (launch(i) enqueues one on the current stream) into a HIP graph,
+    replay it reps times, return microseconds per launch (median over replays)."""
+    launch(0)                               # first call outside capture (device checks, lazy init)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(n_calls):
+                launch(i)
+    torch.cuda.synchronize()
+    per = []
+    with torch.cuda.stream(s):
+        g.replay()                          # warm replay
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            g.replay()
+            e1.record(s)
+            e1.synchronize()
+            per.append(e0.elapsed_time(e1) * 1e3 / n_calls)
+    torch.cuda.synchronize()
+    del g
+    return statistics.median(per)
 
 
-def src_hash(*names) -> str:
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "int4_quantized_linear_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-def traffic_from_profiles(kernel_key: str, current_hash: str):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were taken on
-    the current kernel source; otherwise None."""
-    p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    if not os.path.exists(p):
-        return None
-    try:
-        d = json.load(open(p)).get(kernel_key)
-    except (OSError, ValueError):
-        return None
-    if not d or d.get("source_hash") != current_hash:
-        return None
-    return d.get("bytes_per_launch")
+# --------------------------------------------------------------------------------------------
+# workloads
 
 
 def bench_prefill(cr, wl, torch, steps, warmup):
@@ -103,7 +147,6 @@ def bench_prefill(cr, wl, torch, steps, warmup):
     nw = ring_count(N * K)
     xs = [xd] + [xd.clone() for _ in range(nx - 1)]
     wqs = [wq0] + [wq0.clone() for _ in range(nw - 1)]
-    wss = [ws0] * nw
     xq = torch.empty((M, K), dtype=torch.int8, device=dev)
     xsc = torch.empty((M,), dtype=torch.float32, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -116,14 +159,15 @@ def bench_prefill(cr, wl, torch, steps, warmup):
         cr._call("convrot_quantize_act", xs[i % nx].data_ptr(), cr.CONVROT_DTYPE_BF16, M, K, 256, 8,
                  xq.data_ptr(), xsc.data_ptr(), st.cuda_stream)
         e[1].record(st)
-        cr.linear(None, wqs[i % nw], wss[i % nw], bd, group=256, xq=xq, x_scale=xsc, out=y)
+        cr._call("convrot_linear", None, 0, xq.data_ptr(), xsc.data_ptr(), M, N, K, 256, wqs[i % nw].data_ptr(),
+                 ws0.data_ptr(), bd.data_ptr(), y.data_ptr(), None, 0, st.cuda_stream)
         e[2].record(st)
         return e
 
     wall, marks = timed_loop(step, steps, warmup, torch)
-    t_rq = sum(ev_ms(m[0], m[1]) for m in marks) / steps
-    t_gemm = sum(ev_ms(m[1], m[2]) for m in marks) / steps
-    t_step = sum(ev_ms(m[0], m[2]) for m in marks) / steps
+    t_rq = sum(m[0].elapsed_time(m[1]) for m in marks) / steps
+    t_gemm = sum(m[1].elapsed_time(m[2]) for m in marks) / steps
+    t_step = sum(m[0].elapsed_time(m[2]) for m in marks) / steps
     ops = 2.0 * M * N * K
     rq_bytes = M * K * 2 + M * K + 4 * M
     gemm_bytes = M * K + N * K + 4 * M + 4 * N + 4 * N + 2 * M * N
@@ -133,7 +177,6 @@ def bench_prefill(cr, wl, torch, steps, warmup):
 
 def bench_decode(cr, wl, torch, steps, warmup):
     dev = torch.device("cuda:0")
-    st = torch.cuda.current_stream(dev)
     out = {}
     for (K, N) in wl.DECODE_SHAPES:
         M = wl.DECODE_M
@@ -145,33 +188,41 @@ def bench_decode(cr, wl, torch, steps, warmup):
         xq, xsc = cr.quantize_act(xd, 256, 8)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         wsz = cr.workspace_bytes(M, N, K, 8)
-        ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(wsz, 256), dtype=torch.uint8, device=dev)
 
         def gemv(i):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            e[0].record(st)
             cr._call("convrot_linear", None, 0, xq.data_ptr(), xsc.data_ptr(), M, N, K, 256,
-                     wqs[i % nw].data_ptr(), ws0.data_ptr(), None, y.data_ptr(), ws.data_ptr(), wsz, st.cuda_stream)
-            e[1].record(st)
-            return e
+                     wqs[i % nw].data_ptr(), ws0.data_ptr(), None, y.data_ptr(), ws.data_ptr(), wsz,
+                     torch.cuda.current_stream(dev).cuda_stream)
 
         def e2e(i):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            e[0].record(st)
             cr._call("convrot_linear", xd.data_ptr(), cr.CONVROT_DTYPE_BF16, None, None, M, N, K, 256,
-                     wqs[i % nw].data_ptr(), ws0.data_ptr(), None, y.data_ptr(), ws.data_ptr(), wsz, st.cuda_stream)
-            e[1].record(st)
-            return e
+                     wqs[i % nw].data_ptr(), ws0.data_ptr(), None, y.data_ptr(), ws.data_ptr(), wsz,
+                     torch.cuda.current_stream(dev).cuda_stream)
 
-        _, mg = timed_loop(gemv, steps, warmup, torch)
-        _, me = timed_loop(e2e, steps, warmup, torch)
-        tg = sum(ev_ms(a, b) for a, b in mg) / steps
-        te = sum(ev_ms(a, b) for a, b in me) / steps
+        def eager(fn):
+            st = torch.cuda.current_stream(dev)
+
+            def one(i):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record(st)
+                fn(i)
+                e[1].record(st)
+                return e
+            _, m = timed_loop(one, steps, warmup, torch)
+            return sum(a.elapsed_time(b) for a, b in m) / steps * 1e3
+
+        n_calls = max(nw, 20)
+        tg = graph_time_us(torch, gemv, n_calls, max(steps, 5))
+        te = graph_time_us(torch, e2e, n_calls, max(steps, 5))
+        tg_eager, te_eager = eager(gemv), eager(e2e)
         wbytes = N * K + 4 * N
-        out["K%d_N%d" % (K, N)] = dict(weight_bytes=wbytes, gemv_us=tg * 1e3, e2e_us=te * 1e3,
-                                       weight_GBps=wbytes / (tg * 1e-3) / 1e9,
-                                       frac_hbm=wbytes / (tg * 1e-3) / 1e9 / PEAK_HBM_GBS)
-        log("decode K=%d N=%d: GEMV %.2f us (%.0f GB/s), e2e %.2f us" % (K, N, tg * 1e3, out["K%d_N%d" % (K, N)]["weight_GBps"], te * 1e3))
+        gbs = wbytes / (tg * 1e-6) / 1e9
+        out["K%d_N%d" % (K, N)] = dict(weight_bytes=wbytes, gemv_us=tg, e2e_us=te, weight_GBps=gbs,
+                                       frac_hbm=gbs / PEAK_HBM_GBS, gemv_eager_us=tg_eager, e2e_eager_us=te_eager,
+                                       splits=None, timing="hip graph replay of %d launches" % n_calls)
+        log("decode K=%d N=%d: GEMV %.2f us (%.0f GB/s, %.0f%% of HBM), e2e %.2f us; eager %.2f / %.2f us" % (
+            K, N, tg, gbs, 100 * gbs / PEAK_HBM_GBS, te, tg_eager, te_eager))
         del wqs, wq0
         torch.cuda.empty_cache()
     return out
@@ -189,50 +240,105 @@ def bench_w4a4(cr, wl, torch, steps, warmup):
     xq4, xs4 = cr.quantize_act(xd, 256, 4)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
-    def core(i):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        e[0].record(st)
-        cr.linear_w4a4(None, wq4, ws4, bd, xq=xq4, x_scale=xs4, out=y)
-        e[1].record(st)
-        return e
+    def timed(fn):
+        def one(i):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(st)
+            fn()
+            e[1].record(st)
+            return e
+        _, m = timed_loop(one, steps, warmup, torch)
+        return sum(a.elapsed_time(b) for a, b in m) / steps
 
-    def e2e4(i):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        e[0].record(st)
-        cr.linear_w4a4(xd, wq4, ws4, bd, out=y)
-        e[1].record(st)
-        return e
-
-    def e2e8(i):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        e[0].record(st)
-        cr.linear(xd, wq8, ws8, bd, out=y)
-        e[1].record(st)
-        return e
-
-    _, mc = timed_loop(core, steps, warmup, torch)
-    _, m4 = timed_loop(e2e4, steps, warmup, torch)
-    _, m8 = timed_loop(e2e8, steps, warmup, torch)
-    tc = sum(ev_ms(a, b) for a, b in mc) / steps
-    t4 = sum(ev_ms(a, b) for a, b in m4) / steps
-    t8 = sum(ev_ms(a, b) for a, b in m8) / steps
+    tc = timed(lambda: cr.linear_w4a4(None, wq4, ws4, bd, xq=xq4, x_scale=xs4, out=y))
+    t4 = timed(lambda: cr.linear_w4a4(xd, wq4, ws4, bd, out=y))
+    t8 = timed(lambda: cr.linear(xd, wq8, ws8, bd, out=y))
     ops = 2.0 * M * N * K
     promoted = len(wl.mixed_profile_layers())
     mixed_ms = (240 - promoted) * t4 + promoted * t8
     return dict(M=M, K=K, N=N, gemm_us=tc * 1e3, gemm_tops=ops / (tc * 1e-3) / 1e12,
+                gemm_frac_int8_peak=ops / (tc * 1e-3) / 1e12 / PEAK_INT8_TOPS,
                 e2e_us=t4 * 1e3, e2e_tops=ops / (t4 * 1e-3) / 1e12, w8a8_e2e_us=t8 * 1e3,
                 mixed_profile=dict(layers=240, w8a8_layers=promoted, total_ms=mixed_ms,
                                    effective_tops=240 * ops / (mixed_ms * 1e-3) / 1e12))
 
 
+def bench_stack(cr, wl, torch, layers: int):
+    """All layers' INT8 weights resident; per layer: 4 rotate+quantize of the layer's inputs and
+    the 7 linears on the pre-quantized inputs (q/k/v share one, gate/up share one)."""
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    M = wl.STACK_M
+    log("stack: preparing %d layers of weights and inputs on the device" % layers)
+    t0 = time.perf_counter()
+    W, X = [], []
+    for L in range(layers):
+        mats = {}
+        for i, (name, K, N) in enumerate(wl.STACK_MATRICES):
+            mats[name] = cr.prepare_weight(wl.stack_weight(L, i, N, K, dev), 256, 8)
+        W.append(mats)
+        X.append({inp: wl.stack_acts(L, j, M, K, dev) for j, (inp, K) in enumerate(wl.STACK_INPUTS)})
+    torch.cuda.synchronize()
+    log("stack: prepared in %.1f s (%.1f GB of INT8 weights)" % (
+        time.perf_counter() - t0, sum(w[0].numel() for m in W for w in m.values()) / 1e9))
+    xq = {inp: torch.empty((M, K), dtype=torch.int8, device=dev) for inp, K in wl.STACK_INPUTS}
+    xs = {inp: torch.empty((M,), dtype=torch.float32, device=dev) for inp, _ in wl.STACK_INPUTS}
+    ys = {name: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for name, _, N in wl.STACK_MATRICES}
+    kdim = dict(wl.STACK_INPUTS)
+
+    def layer(L):
+        for inp, K in wl.STACK_INPUTS:
+            cr._call("convrot_quantize_act", X[L][inp].data_ptr(), cr.CONVROT_DTYPE_BF16, M, K, 256, 8,
+                     xq[inp].data_ptr(), xs[inp].data_ptr(), st.cuda_stream)
+        for name, K, N in wl.STACK_MATRICES:
+            inp = wl.STACK_INPUT_OF[name]
+            assert kdim[inp] == K
+            wq, sw = W[L][name]
+            cr._call("convrot_linear", None, 0, xq[inp].data_ptr(), xs[inp].data_ptr(), M, N, K, 256, wq.data_ptr(),
+                     sw.data_ptr(), None, ys[name].data_ptr(), None, 0, st.cuda_stream)
+
+    ops = sum(2.0 * M * N * K for _, K, N in wl.STACK_MATRICES)
+    per_pass = []
+    for rep in range(3):                      # pass 0 warms up
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(layers + 1)]
+        ev[0].record(st)
+        for L in range(layers):
+            layer(L)
+            ev[L + 1].record(st)
+        torch.cuda.synchronize()
+        if rep:
+            per_pass.append([ev[i].elapsed_time(ev[i + 1]) for i in range(layers)])
+    per_layer = [t for p in per_pass for t in p]
+    med = statistics.median(per_layer)
+    total = statistics.median([sum(p) for p in per_pass])
+    res = dict(layers=layers, M=M, ops_per_layer=ops, median_layer_us=med * 1e3,
+               median_layer_tops=ops / (med * 1e-3) / 1e12, total_ms=total,
+               frac_int8_peak=ops / (med * 1e-3) / 1e12 / PEAK_INT8_TOPS)
+    del W, X
+    torch.cuda.empty_cache()
+    return res
+
+
+def copy_probe(torch):
+    """Plain device copy of COPY_PROBE_BYTES (5 launches): the calibration kernel for counters."""
+    dev = torch.device("cuda:0")
+    n = COPY_PROBE_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy probe: 5 copies of %d bytes" % COPY_PROBE_BYTES)
+
+
 def cpu_baseline(wl, torch):
-    """The oracle as it stands on a bounded sample of the prefill workload: S tokens against R
-    weight rows (weights prepared untimed, as on the GPU); timed = rotate+quantize the tokens,
-    integer GEMM, dequant."""
+    """The oracle as it stands on a bounded sample of the prefill workload: all S = 4096 tokens
+    against the first R = 8192 of the 16128 output channels (half the work); weights prepared
+    untimed as on the GPU; timed = rotate+quantize the tokens, integer GEMM, dequant."""
     import numpy as np
 
     from oracle import oracle as orc
-    S, R = 128, 2048
+    S, R = 4096, 8192
     x, w, b = wl.prefill_inputs()
     xs = x[:S].double().numpy()
     wr = w[:R].double().numpy()
@@ -247,14 +353,95 @@ def cpu_baseline(wl, torch):
     K = xs.shape[1]
     ops = 2.0 * S * R * K
     return dict(value=ops / dt / 1e12, unit="TOP/s", cores=orc.num_threads(), kind="oracle",
-                sample="%d tokens x %d output channels of the 4096x5376x16128 prefill linear "
-                       "(rotate+quantize tokens, int GEMM, dequant; weights prepared untimed); %.1f s" % (S, R, dt))
+                sample="%d tokens x %d of 16128 output channels of the 4096x5376x16128 prefill linear "
+                       "(rotate+quantize tokens, int64-checked integer GEMM, fp64 dequant; weights prepared "
+                       "untimed): %.3g ops in %.1f s" % (S, R, ops, dt))
+
+
+# --------------------------------------------------------------------------------------------
+# counter summary
+
+
+def _counter_rows(path):
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def _kernel_key(name: str):
+    if "gemm_i8_kernel" in name:
+        return "gemm_i8"
+    if "rotate_quant_kernel" in name:
+        return "rotate_quant"
+    if "gemv_i8_kernel" in name:
+        return "gemv_i8"
+    if "gemm_w4a4" in name:
+        return "gemm_w4a4"
+    if "copyBuffer" in name:
+        return "copy"
+    return None
+
+
+def _per_dispatch_kib(path, counter):
+    acc = {}
+    for name, cname, v in _counter_rows(path):
+        k = _kernel_key(name)
+        if k and cname == counter:
+            acc.setdefault(k, []).append(v)
+    return {k: statistics.median(v) for k, v in acc.items()}
+
+
+PMC_COMMANDS = [
+    "cd /tmp && export TMPDIR=/tmp && cd <repo>",
+    "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run --output-format csv -- "
+    "python bench.py --only prefill --steps 3 --warmup 1 --no-cpu-baseline",
+    "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run --output-format csv -- "
+    "python bench.py --only prefill --steps 3 --warmup 1 --no-cpu-baseline",
+    "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_cfetch -o run --output-format csv -- python bench.py --only copy",
+    "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_cwrite -o run --output-format csv -- python bench.py --only copy",
+    "python bench.py --pmc-summary gpurun_out/pmc_fetch/run_counter_collection.csv "
+    "gpurun_out/pmc_write/run_counter_collection.csv gpurun_out/pmc_cfetch/run_counter_collection.csv "
+    "gpurun_out/pmc_cwrite/run_counter_collection.csv",
+]
+
+
+def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    f = _per_dispatch_kib(fetch_csv, "FETCH_SIZE")
+    w = _per_dispatch_kib(write_csv, "WRITE_SIZE")
+    cf = _per_dispatch_kib(copy_fetch_csv, "FETCH_SIZE")["copy"]
+    cw = _per_dispatch_kib(copy_write_csv, "WRITE_SIZE")["copy"]
+    kib = COPY_PROBE_BYTES / 1024.0
+    ff, fw = kib / cf, kib / cw
+    out = {"commands": PMC_COMMANDS,
+           "calibration": {"kernel": "device copy (__amd_rocclr_copyBuffer) of %d bytes" % COPY_PROBE_BYTES,
+                           "fetch_kib_per_dispatch": cf, "write_kib_per_dispatch": cw,
+                           "fetch_factor": ff, "write_factor": fw},
+           "kernels": {}}
+    for k in sorted(set(f) & set(w)):
+        if k == "copy":
+            continue
+        fb, wb = f[k] * 1024 * ff, w[k] * 1024 * fw
+        out["kernels"][k + "_prefill" if k in ("gemm_i8", "rotate_quant") else k] = {
+            "source_hash": src_hash(KERNEL_SOURCES[k]), "fetch_bytes": fb, "write_bytes": wb,
+            "bytes_per_launch": fb + wb, "fetch_kib_raw": f[k], "write_kib_raw": w[k]}
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+# --------------------------------------------------------------------------------------------
 
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU only: this library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
     import torch
@@ -264,6 +451,9 @@ def main():
     cr.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.only == "copy":
+        copy_probe(torch)
+        return
     res = {}
     if args.only in ("all", "prefill"):
         res["prefill"] = bench_prefill(cr, wl, torch, args.steps, args.warmup)
@@ -277,6 +467,11 @@ def main():
         res["w4a4"] = bench_w4a4(cr, wl, torch, args.steps, args.warmup)
         log("w4a4: GEMM %.1f us (%.0f TOP/s), e2e %.1f us" % (res["w4a4"]["gemm_us"], res["w4a4"]["gemm_tops"],
                                                              res["w4a4"]["e2e_us"]))
+        torch.cuda.empty_cache()
+    if args.only in ("all", "stack"):
+        res["stack"] = bench_stack(cr, wl, torch, args.stack_layers)
+        log("stack: median layer %.1f us (%.0f TOP/s)" % (res["stack"]["median_layer_us"],
+                                                         res["stack"]["median_layer_tops"]))
     cpu = None
     if not args.no_cpu_baseline and args.only in ("all", "prefill"):
         cpu = cpu_baseline(wl, torch)
@@ -294,21 +489,30 @@ def main():
             "value": p["ops"] / (p["step_ms"] * 1e-3) / 1e12, "unit": "TOP/s", "ms_per_step": p["step_ms"],
             "wall_ms_per_step": p["wall_ms"],
             "config": {"workload": "ConvRot W8A8 linear, prefill attn.qkv_proj-shaped: M=4096 tokens, K=5376 "
-                                   "(21 groups of 256), N=16128; bf16 x with 0.5% outlier channels x50; bias; bf16 out",
+                                   "(21 groups of 256), N=16128; bf16 x N(0,1) with 0.5% outlier channels x50; "
+                                   "W N(0,0.02); fp32 bias; bf16 out; step = rotate+quantize x, then GEMM+dequant",
                        "M": p["M"], "K": p["K"], "N": p["N"], "group": 256},
             "roofline": {"bound": "mfma", "kernel": "gemm_i8 (int8 MFMA GEMM + dequant epilogue)",
                          "achieved": gemm_tops, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                          "frac": gemm_tops / PEAK_INT8_TOPS,
-                         "traffic": traffic_from_profiles("gemm_i8_prefill", h), "source_hash": h},
+                         "traffic": traffic_from_profiles("gemm_i8_prefill", h),
+                         "algorithmic_bytes": p["gemm_bytes"], "source_hash": h},
             "kernels": {"rotate_quant_us": p["rq_ms"] * 1e3, "rotate_quant_GBps": rq_gbs,
                         "rotate_quant_frac_hbm": rq_gbs / PEAK_HBM_GBS,
+                        "rotate_quant_traffic": traffic_from_profiles("rotate_quant_prefill",
+                                                                      src_hash("rotate_quant.hip")),
                         "gemm_us": p["gemm_ms"] * 1e3, "gemm_TOPs": gemm_tops,
                         "gemm_frac_int8_peak": gemm_tops / PEAK_INT8_TOPS},
         })
+    else:
+        line.update({"value": None, "unit": "TOP/s", "ms_per_step": None,
+                     "config": {"workload": "partial run (--only %s)" % args.only}})
     if "decode" in res:
         line["decode_m12"] = res["decode"]
     if "w4a4" in res:
         line["w4a4"] = res["w4a4"]
+    if "stack" in res:
+        line["layer_stack"] = res["stack"]
     line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 

@@ -132,3 +132,33 @@ def ragged_case(M: int, K: int, N: int, seed: int, dtype=torch.bfloat16, outlier
     if dtype == torch.bfloat16:
         return to_bf16(x), to_bf16(w), torch.from_numpy(b)
     return torch.from_numpy(x), torch.from_numpy(w), torch.from_numpy(b)
+
+
+def _device_generator(cfg: int, layer: int, role: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([cfg, layer, role]).generate_state(1, dtype=np.uint64)[0] >> 1))
+    return g
+
+
+def stack_weight(layer: int, idx: int, N: int, K: int, device, std: float = 0.02) -> torch.Tensor:
+    """Layer-stack weight drawn on the device (31 GB of them would take minutes on the host):
+    bf16 N(0, std), seeded per (layer, matrix)."""
+    g = _device_generator(CFG_STACK, layer * 16 + idx, ROLE_W, device)
+    return (torch.randn(N, K, generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
+
+
+def stack_acts(layer: int, key: int, M: int, K: int, device, frac: float = 0.01, factor: float = 30.0
+               ) -> torch.Tensor:
+    """Layer-stack activation drawn on the device: Student-t (nu = 4) as Z / sqrt(V / 4) with V the
+    sum of 4 squared standard normals, round(frac*K) channels scaled by `factor`, bf16; a fresh
+    seed per (layer, input)."""
+    g = _device_generator(CFG_STACK, layer * 16 + key, ROLE_X, device)
+    z = torch.randn(M, K, generator=g, device=device, dtype=torch.float32)
+    v = torch.zeros(M, K, device=device, dtype=torch.float32)
+    for _ in range(4):
+        v += torch.randn(M, K, generator=g, device=device, dtype=torch.float32).square_()
+    x = z / torch.sqrt(v * 0.25)
+    go = _device_generator(CFG_STACK, layer * 16 + key, ROLE_OUTLIER, device)
+    ch = torch.randperm(K, generator=go, device=device)[: int(round(frac * K))]
+    x[:, ch] *= factor
+    return x.to(torch.bfloat16)
