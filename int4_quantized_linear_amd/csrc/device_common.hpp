@@ -14,6 +14,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
@@ -39,6 +40,35 @@ __device__ __forceinline__ float dpp_xor2(float v)
 {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)); // [2,3,0,1]
 }
+
+// x[i] += c * x[i] of the partner lane (lane ^ 1 for QUAD_PERM "[1,0,3,2]", lane ^ 2 for
+// "[2,3,0,1]"), for 8 values: one v_fmac_f32 per value with its first source read through DPP.
+// (The compiler keeps a separate v_mov_b32_dpp for the tied-accumulator fmac.)  The leading
+// s_nop covers the DPP read-after-VALU-write hazard for all eight: inside the block each
+// instruction reads only the register it alone writes.
+#define CONVROT_FMAC_DPP8(QUAD_PERM)                                                                        \
+    __device__ __forceinline__ void fmac_dpp8_##QUAD_PERM##_(float (&x)[8], float c)                       \
+    {                                                                                                       \
+        asm volatile("s_nop 1\n\t"                                                                         \
+                     "v_fmac_f32_dpp %0, %0, %8 quad_perm:" QP_##QUAD_PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                     "v_fmac_f32_dpp %1, %1, %8 quad_perm:" QP_##QUAD_PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                     "v_fmac_f32_dpp %2, %2, %8 quad_perm:" QP_##QUAD_PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                     "v_fmac_f32_dpp %3, %3, %8 quad_perm:" QP_##QUAD_PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                     "v_fmac_f32_dpp %4, %4, %8 quad_perm:" QP_##QUAD_PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                     "v_fmac_f32_dpp %5, %5, %8 quad_perm:" QP_##QUAD_PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                     "v_fmac_f32_dpp %6, %6, %8 quad_perm:" QP_##QUAD_PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                     "v_fmac_f32_dpp %7, %7, %8 quad_perm:" QP_##QUAD_PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1" \
+                     : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),    \
+                       "+v"(x[7])                                                                           \
+                     : "v"(c));                                                                             \
+    }
+#define QP_xor1 "[1,0,3,2]"
+#define QP_xor2 "[2,3,0,1]"
+CONVROT_FMAC_DPP8(xor1)
+CONVROT_FMAC_DPP8(xor2)
+#undef CONVROT_FMAC_DPP8
+#undef QP_xor1
+#undef QP_xor2
 
 // Exchange the upper 32 lanes of `a` with the lower 32 lanes of `b` (v_permlane32_swap):
 // afterwards a = [a_lo | b_lo], b = [a_hi | b_hi].

@@ -33,10 +33,12 @@ struct RQParams {
     int64_t rows;
     int K;
     int slots_per_row;   // ceil(K / 256)
-    int rows_per_wg;     // rows handled by one workgroup (<= 64)
-    int log2g;           // rotation group = 2^log2g channels (0..8)
+    int rows_per_wg;     // rows handled by one workgroup per iteration (<= 64)
+    int ngroups;         // ceil(rows / rows_per_wg)
     float cg;            // 1/sqrt(g) in fp32
 };
+
+constexpr uint32_t OOB = 0x80000000u;   // buffer offset past num_records: loads read 0, stores drop
 
 __device__ __forceinline__ void bfly(float &a, float &b)
 {
@@ -45,199 +47,244 @@ __device__ __forceinline__ void bfly(float &a, float &b)
     a = s;
 }
 
-template <bool F32IN, int BITS, int SETS>
+// LG = log2 of the rotation group (0..8), a template parameter so that the butterfly stages are
+// straight-line code.  All global accesses are buffer instructions whose out-of-range lanes get
+// an out-of-bounds offset (loads return 0, stores are dropped): no branches around them, so the
+// loads of a wavefront are all in flight together.
+//
+// Persistent: a workgroup walks row groups blockIdx.x, blockIdx.x + gridDim.x, ... and issues
+// the raw loads of its next row group before it transforms the current one, so HBM reads stay
+// in flight while the VALU works (without this, all waves would load, then all compute).
+template <bool F32IN, int BITS, int SETS, int LG>
 __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
 {
-    __shared__ unsigned smax[64];
+    __shared__ unsigned smax[2][64];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nwave = blockDim.x >> 6;
     const int qd = lane & 3, h = lane >> 5, sl = (lane >> 2) & 7;
-    if (threadIdx.x < 64) smax[threadIdx.x] = 0u;
+    if (threadIdx.x < 64) smax[0][threadIdx.x] = 0u;
 
-    float v[SETS][4][8];
+    constexpr int ES = F32IN ? 4 : 2;                       // input element bytes
+    constexpr int NL = F32IN ? 2 : 1;                       // 16-byte loads per chunk
+    const int K = p.K;
+    const int R = p.rows_per_wg;
+
+    // Static slot geometry: slot -> (row within the group, 256-channel block); element offset
+    // of each chunk inside the row group, or OOB for slots/channels past the row or the group.
     int rr[SETS], jj[SETS];
-    bool ok[SETS];
-    int64_t rowv[SETS];
-
+    uint32_t kbase[SETS][4];
 #pragma unroll
     for (int s = 0; s < SETS; ++s) {
         const int slot = (s * nwave + wave) * 8 + sl;
         rr[s] = slot / p.slots_per_row;
         jj[s] = slot - rr[s] * p.slots_per_row;
-        rowv[s] = (int64_t)blockIdx.x * p.rows_per_wg + rr[s];
-        ok[s] = rr[s] < p.rows_per_wg && rowv[s] < p.rows;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int k = 256 * jj[s] + 64 * r + 32 * h + 8 * qd;
-            if (ok[s] && k < p.K) {
-                if constexpr (F32IN) {
-                    const v4f *src = reinterpret_cast<const v4f *>(
-                        static_cast<const float *>(p.x) + rowv[s] * (int64_t)p.K + k);
-                    const v4f a = __builtin_nontemporal_load(src);
-                    const v4f b = __builtin_nontemporal_load(src + 1);
-                    v[s][r][0] = a.x; v[s][r][1] = a.y; v[s][r][2] = a.z; v[s][r][3] = a.w;
-                    v[s][r][4] = b.x; v[s][r][5] = b.y; v[s][r][6] = b.z; v[s][r][7] = b.w;
-                } else {
-                    const v4u *src = reinterpret_cast<const v4u *>(
-                        static_cast<const uint16_t *>(p.x) + rowv[s] * (int64_t)p.K + k);
-                    const v4u a = __builtin_nontemporal_load(src);
-                    v[s][r][0] = bf16lo_to_f32(a.x); v[s][r][1] = bf16hi_to_f32(a.x);
-                    v[s][r][2] = bf16lo_to_f32(a.y); v[s][r][3] = bf16hi_to_f32(a.y);
-                    v[s][r][4] = bf16lo_to_f32(a.z); v[s][r][5] = bf16hi_to_f32(a.z);
-                    v[s][r][6] = bf16lo_to_f32(a.w); v[s][r][7] = bf16hi_to_f32(a.w);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[s][r][e] = 0.0f;
-            }
+            kbase[s][r] = (rr[s] < R && k < K) ? (uint32_t)(rr[s] * K + k) : OOB;
         }
     }
 
-    // ---- unnormalised Walsh-Hadamard butterflies on channel bits < log2g (uniform branches)
-    const int lg = p.log2g;
-#pragma unroll
-    for (int s = 0; s < SETS; ++s) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-#pragma unroll
-            for (int b = 0; b < 3; ++b) {
-                if (lg > b) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (!(e & (1 << b))) bfly(v[s][r][e], v[s][r][e | (1 << b)]);
-                }
-            }
-        }
-        // channel bits 3 and 4: partner is lane ^ 1 / lane ^ 2.  The lower lane keeps a + b,
-        // the upper lane keeps a - b:  out = partner + c * self with c = -1 on the upper lane.
-        if (lg > 3) {
-            const float c = (qd & 1) ? -1.0f : 1.0f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[s][r][e] = __builtin_fmaf(v[s][r][e], c, dpp_xor1(v[s][r][e]));
-        }
-        if (lg > 4) {
-            const float c = (qd & 2) ? -1.0f : 1.0f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[s][r][e] = __builtin_fmaf(v[s][r][e], c, dpp_xor2(v[s][r][e]));
-        }
-        // channel bits 6 and 7: chunk registers
-        if (lg > 6) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) { bfly(v[s][0][e], v[s][1][e]); bfly(v[s][2][e], v[s][3][e]); }
-        }
-        if (lg > 7) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) { bfly(v[s][0][e], v[s][2][e]); bfly(v[s][1][e], v[s][3][e]); }
-        }
-        // channel bit 5: swap it with chunk bit 0 (channel bit 6) between lane halves, then
-        // butterfly in registers.  Afterwards v[s][2*r1 + c5][e] holds channel bit 5 = c5 and
-        // channel bit 6 = lane bit 5.
-        if (lg > 5) {
-#pragma unroll
-            for (int r1 = 0; r1 < 2; ++r1)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    swap32f(v[s][2 * r1][e], v[s][2 * r1 + 1][e]);
-                    bfly(v[s][2 * r1][e], v[s][2 * r1 + 1][e]);
-                }
-        }
-    }
-
-    // ---- absmax: per slot over its 8 lanes (lane bits 0, 1 and 5)
-    float m[SETS];
-#pragma unroll
-    for (int s = 0; s < SETS; ++s) {
-        float a = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(v[s][r][e]));
-        a = __builtin_fmaxf(a, dpp_xor1(a));
-        a = __builtin_fmaxf(a, dpp_xor2(a));
-        uint32_t lo = __float_as_uint(a), hi = lo;
-        swap32(lo, hi);
-        m[s] = __builtin_fmaxf(__uint_as_float(lo), __uint_as_float(hi));
-    }
-
-    float mult[SETS];
-    if constexpr (BITS == 8) {
-        // row absmax across slots/waves through LDS (non-negative float bits order like uints)
-        __syncthreads();
+    v4u raw[SETS][4][NL];
+    auto issue = [&](int it) {
+        const int64_t row0 = (int64_t)it * R;
+        const int nrows = (int)(p.rows - row0 < R ? p.rows - row0 : R);
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(static_cast<const uint8_t *>(p.x) + row0 * K * ES), (short)0, nrows * K * ES,
+            0x00020000);
 #pragma unroll
         for (int s = 0; s < SETS; ++s)
-            if (ok[s] && qd == 0 && h == 0) atomicMax(&smax[rr[s]], __float_as_uint(m[s]));
-        __syncthreads();
 #pragma unroll
-        for (int s = 0; s < SETS; ++s) {
-            const float amax = __uint_as_float(smax[rr[s] < 64 ? rr[s] : 63]);
-            const float sc = (amax * p.cg) / 127.0f;
-            mult[s] = sc > 0.0f ? p.cg / sc : 0.0f;
-            if (ok[s] && jj[s] == 0 && qd == 0 && h == 0) static_cast<float *>(p.scale)[rowv[s]] = sc;
-        }
-    } else {
-        // one fp16 scale per 256-channel group (= slot)
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int s = 0; s < SETS; ++s) {
-            const __half sh = __float2half_rn((m[s] * p.cg) / 7.0f);
-            const float sc = __half2float(sh);
-            mult[s] = sc > 0.0f ? p.cg / sc : 0.0f;
-            if (ok[s] && qd == 0 && h == 0)
-                static_cast<__half *>(p.scale)[(int64_t)jj[s] * p.rows + rowv[s]] = sh;
-        }
-    }
+                for (int l = 0; l < NL; ++l) {
+                    // rows past the end lie past num_records: they read zeros.  Read once:
+                    // nontemporal (aux bit 1).
+                    const uint32_t o = kbase[s][r] == OOB ? OOB : kbase[s][r] * ES + 16 * l;
+                    raw[s][r][l] = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 2);
+                }
+    };
 
-    // ---- codes, back to the load layout, store
+    // Prefetching holds a second copy of the raw row data: only for SETS == 1 (K <= 32768); the
+    // wider rows would not fit the registers of a 1024-thread workgroup.
+    constexpr bool PF = SETS == 1;
+    int it = blockIdx.x;
+    int par = 0;
+    if (PF && it < p.ngroups) issue(it);
+    for (; it < p.ngroups; it += gridDim.x, par ^= 1) {
+        if constexpr (!PF) issue(it);
+        const int64_t row0 = (int64_t)it * R;
+        const int nrows = (int)(p.rows - row0 < R ? p.rows - row0 : R);
+        float v[SETS][4][8];
 #pragma unroll
-    for (int s = 0; s < SETS; ++s) {
-        if constexpr (BITS == 8) {
-            uint32_t c[4][2];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                uint32_t t[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) t[e] = rne_bits(v[s][r][e], mult[s]);
-                c[r][0] = pack4_i8(t[0], t[1], t[2], t[3]);
-                c[r][1] = pack4_i8(t[4], t[5], t[6], t[7]);
-            }
-            if (lg > 5) {
-#pragma unroll
-                for (int r1 = 0; r1 < 2; ++r1) { swap32(c[2 * r1][0], c[2 * r1 + 1][0]); swap32(c[2 * r1][1], c[2 * r1 + 1][1]); }
-            }
+        for (int s = 0; s < SETS; ++s)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int k = 256 * jj[s] + 64 * r + 32 * h + 8 * qd;
-                if (ok[s] && k < p.K) {
-                    uint2 *dst = reinterpret_cast<uint2 *>(static_cast<int8_t *>(p.q) + rowv[s] * (int64_t)p.K + k);
-                    *dst = make_uint2(c[r][0], c[r][1]);
+                if constexpr (F32IN) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[s][r][e] = __uint_as_float(raw[s][r][e >> 2][e & 3]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[s][r][2 * e] = bf16lo_to_f32(raw[s][r][0][e]);
+                        v[s][r][2 * e + 1] = bf16hi_to_f32(raw[s][r][0][e]);
+                    }
                 }
             }
+        if (PF && it + (int)gridDim.x < p.ngroups) issue(it + gridDim.x);   // prefetch the next group
+        bool ok[SETS];
+#pragma unroll
+        for (int s = 0; s < SETS; ++s) ok[s] = rr[s] < nrows;
+
+        // ---- unnormalised Walsh-Hadamard butterflies on channel bits < LG
+#pragma unroll
+        for (int s = 0; s < SETS; ++s) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                for (int b = 0; b < 3; ++b) {
+                    if (LG > b) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (!(e & (1 << b))) bfly(v[s][r][e], v[s][r][e | (1 << b)]);
+                    }
+                }
+            }
+            // channel bits 6 and 7: chunk registers
+            if constexpr (LG > 6) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { bfly(v[s][0][e], v[s][1][e]); bfly(v[s][2][e], v[s][3][e]); }
+            }
+            if constexpr (LG > 7) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { bfly(v[s][0][e], v[s][2][e]); bfly(v[s][1][e], v[s][3][e]); }
+            }
+            // channel bit 5: swap it with chunk bit 0 (channel bit 6) between lane halves, then
+            // butterfly in registers.  Afterwards v[s][2*r1 + c5][e] holds channel bit 5 = c5 and
+            // channel bit 6 = lane bit 5.
+            if constexpr (LG > 5) {
+#pragma unroll
+                for (int r1 = 0; r1 < 2; ++r1)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        swap32f(v[s][2 * r1][e], v[s][2 * r1 + 1][e]);
+                        bfly(v[s][2 * r1][e], v[s][2 * r1 + 1][e]);
+                    }
+            }
+            // channel bits 3 and 4, last: partner is lane ^ 1 / lane ^ 2.  Each stage is one
+            // v_fmac_f32_dpp per value: self + partner * c, c = +1 on the lower lane (a + b,
+            // correct) and -1 on the upper lane (b - a, the negated result).
+            // Running the two lane stages after all others keeps that sign error out of every
+            // other butterfly: the final value of a lane is off by the sign (-1)^(bit0 ^ bit1)
+            // of its quad position, which is folded into the quantization multiplier below and
+            // does not change |v|.
+            if constexpr (LG > 3) {
+                const float c = (qd & 1) ? -1.0f : 1.0f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) fmac_dpp8_xor1_(v[s][r], c);
+            }
+            if constexpr (LG > 4) {
+                const float c = (qd & 2) ? -1.0f : 1.0f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) fmac_dpp8_xor2_(v[s][r], c);
+            }
+        }
+
+        // ---- absmax: per slot over its 8 lanes (lane bits 0, 1 and 5)
+        float m[SETS];
+#pragma unroll
+        for (int s = 0; s < SETS; ++s) {
+            float a = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(v[s][r][e]));
+            a = __builtin_fmaxf(a, dpp_xor1(a));
+            a = __builtin_fmaxf(a, dpp_xor2(a));
+            uint32_t lo = __float_as_uint(a), hi = lo;
+            swap32(lo, hi);
+            m[s] = __builtin_fmaxf(__uint_as_float(lo), __uint_as_float(hi));
+        }
+
+        // sign left on this lane's values by the lane-exchange butterflies
+        const float lsign = (((LG > 3 ? qd : 0) ^ (LG > 4 ? qd >> 1 : 0)) & 1) ? -1.0f : 1.0f;
+        float mult[SETS];
+        if constexpr (BITS == 8) {
+            // row absmax across slots/waves through LDS (non-negative float bits order like uints).
+            // smax[par] was cleared before the previous iteration's first barrier; the other
+            // buffer, last read before this barrier, is cleared for the next iteration.
+            __syncthreads();
+            if (threadIdx.x < 64) smax[par ^ 1][threadIdx.x] = 0u;
+#pragma unroll
+            for (int s = 0; s < SETS; ++s)
+                if (ok[s] && qd == 0 && h == 0) atomicMax(&smax[par][rr[s]], __float_as_uint(m[s]));
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < SETS; ++s) {
+                const float amax = __uint_as_float(smax[par][rr[s] < 64 ? rr[s] : 63]);
+                const float sc = (amax * p.cg) / 127.0f;
+                mult[s] = sc > 0.0f ? lsign * (p.cg / sc) : 0.0f;
+                if (ok[s] && jj[s] == 0 && qd == 0 && h == 0) static_cast<float *>(p.scale)[row0 + rr[s]] = sc;
+            }
         } else {
-            uint32_t c[4];
+            // one fp16 scale per 256-channel group (= slot)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                uint32_t t[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) t[e] = rne_bits(v[s][r][e], mult[s]);
-                c[r] = pack8_i4(t);
+            for (int s = 0; s < SETS; ++s) {
+                const __half sh = __float2half_rn((m[s] * p.cg) / 7.0f);
+                const float sc = __half2float(sh);
+                mult[s] = sc > 0.0f ? lsign * (p.cg / sc) : 0.0f;
+                if (ok[s] && qd == 0 && h == 0)
+                    static_cast<__half *>(p.scale)[(int64_t)jj[s] * p.rows + row0 + rr[s]] = sh;
             }
-            if (lg > 5) {
-                swap32(c[0], c[1]);
-                swap32(c[2], c[3]);
-            }
+        }
+
+        // ---- codes, back to the load layout, store (rows past the group's end lie past
+        // num_records and are dropped)
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<uint8_t *>(p.q) + (BITS == 8 ? row0 * K : row0 * (K / 2)), (short)0,
+            BITS == 8 ? nrows * K : nrows * (K / 2), 0x00020000);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int k = 256 * jj[s] + 64 * r + 32 * h + 8 * qd;
-                if (ok[s] && k < p.K)
-                    *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(p.q) + rowv[s] * (int64_t)(p.K / 2) + k / 2) = c[r];
+        for (int s = 0; s < SETS; ++s) {
+            if constexpr (BITS == 8) {
+                uint32_t c[4][2];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    uint32_t t[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) t[e] = rne_bits(v[s][r][e], mult[s]);
+                    c[r][0] = pack4_i8(t[0], t[1], t[2], t[3]);
+                    c[r][1] = pack4_i8(t[4], t[5], t[6], t[7]);
+                }
+                if constexpr (LG > 5) {
+#pragma unroll
+                    for (int r1 = 0; r1 < 2; ++r1) { swap32(c[2 * r1][0], c[2 * r1 + 1][0]); swap32(c[2 * r1][1], c[2 * r1 + 1][1]); }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    __builtin_amdgcn_raw_buffer_store_b64(v2u{c[r][0], c[r][1]}, rq, kbase[s][r], 0, 0);
+            } else {
+                uint32_t c[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    uint32_t t[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) t[e] = rne_bits(v[s][r][e], mult[s]);
+                    c[r] = pack8_i4(t);
+                }
+                if constexpr (LG > 5) {
+                    swap32(c[0], c[1]);
+                    swap32(c[2], c[3]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    __builtin_amdgcn_raw_buffer_store_b32(c[r], rq, kbase[s][r] == OOB ? OOB : kbase[s][r] / 2, 0, 0);
             }
         }
     }
 }
+
+constexpr int RQ_WAVES_PER_CU = 16;
 
 // Host-side launch geometry: rows per workgroup and wavefronts per workgroup so that the
 // 8 slots per wavefront are used as fully as possible (<= 16 wavefronts, <= 64 rows).
@@ -260,6 +307,38 @@ static void rq_geometry(int64_t rows, int K, int &rows_per_wg, int &waves, int &
     }
 }
 
+template <bool F32, int B, int SS>
+static void rq_launch_lg(int log2g, dim3 grid, dim3 block, hipStream_t stream, const RQParams &p)
+{
+    switch (log2g) {
+    case 0: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 0>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 1>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 2>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 3>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 4>), grid, block, 0, stream, p); break;
+    case 5: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 5>), grid, block, 0, stream, p); break;
+    case 6: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 6>), grid, block, 0, stream, p); break;
+    case 7: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 7>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 8>), grid, block, 0, stream, p); break;
+    }
+}
+
+template <bool F32, int B>
+static void rq_launch(int sets, int log2g, dim3 grid, dim3 block, hipStream_t stream, const RQParams &p)
+{
+    if (sets == 1) rq_launch_lg<F32, B, 1>(log2g, grid, block, stream, p);
+    else if (sets == 2) rq_launch_lg<F32, B, 2>(log2g, grid, block, stream, p);
+    else rq_launch_lg<F32, B, 4>(log2g, grid, block, stream, p);
+}
+
+template <bool F32, int B>
+static void rq_launch_g256(int sets, dim3 grid, dim3 block, hipStream_t stream, const RQParams &p)
+{
+    if (sets == 1) hipLaunchKernelGGL((rotate_quant_kernel<F32, B, 1, 8>), grid, block, 0, stream, p);
+    else if (sets == 2) hipLaunchKernelGGL((rotate_quant_kernel<F32, B, 2, 8>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((rotate_quant_kernel<F32, B, 4, 8>), grid, block, 0, stream, p);
+}
+
 hipError_t launch_rotate_quant(const void *x, bool x_f32, int64_t rows, int K, int log2g, int bits, void *q,
                                void *scale, hipStream_t stream)
 {
@@ -274,23 +353,26 @@ hipError_t launch_rotate_quant(const void *x, bool x_f32, int64_t rows, int K, i
     p.K = K;
     p.slots_per_row = (K + 255) / 256;
     p.rows_per_wg = R;
-    p.log2g = log2g;
+    p.ngroups = (int)((rows + R - 1) / R);
     p.cg = (float)(1.0 / __builtin_sqrt((double)(1 << log2g)));
-    const dim3 grid((unsigned)((rows + R - 1) / R)), block(64 * W);
-#define RQ_LAUNCH(F32, B, SS) hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS>), grid, block, 0, stream, p)
-#define RQ_SETS(F32, B)                  \
-    do {                                 \
-        if (S == 1) RQ_LAUNCH(F32, B, 1); \
-        else if (S == 2) RQ_LAUNCH(F32, B, 2); \
-        else RQ_LAUNCH(F32, B, 4);       \
-    } while (0)
+    static const int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            n = 256;
+        return n > 0 ? n : 256;
+    }();
+    // persistent grid: about RQ_WAVES_PER_CU resident wavefronts per CU, each workgroup looping
+    const int per_cu = RQ_WAVES_PER_CU / W > 1 ? RQ_WAVES_PER_CU / W : 1;
+    const int64_t g = (int64_t)cus * per_cu < p.ngroups ? (int64_t)cus * per_cu : p.ngroups;
+    const dim3 grid((unsigned)g), block(64 * W);
+    // INT4 always uses group 256 (checked by the C-ABI layer)
     if (x_f32) {
-        if (bits == 8) RQ_SETS(true, 8); else RQ_SETS(true, 4);
+        if (bits == 8) rq_launch<true, 8>(S, log2g, grid, block, stream, p);
+        else rq_launch_g256<true, 4>(S, grid, block, stream, p);
     } else {
-        if (bits == 8) RQ_SETS(false, 8); else RQ_SETS(false, 4);
+        if (bits == 8) rq_launch<false, 8>(S, log2g, grid, block, stream, p);
+        else rq_launch_g256<false, 4>(S, grid, block, stream, p);
     }
-#undef RQ_SETS
-#undef RQ_LAUNCH
     return hipGetLastError();
 }
 
