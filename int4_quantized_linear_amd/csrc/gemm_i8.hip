@@ -15,17 +15,21 @@
 //    L2.  8 wavefronts (2 per SIMD, so one covers the other's waits) in 2(N) x 4(M) each own a
 //    128x64 sub-tile as 4x2 blocks of v_mfma_i32_32x32x32_i8 (128 int32 accumulators per lane,
 //    in AGPRs, leaving room for a spill-free epilogue);
-//  * K is streamed 64 bytes per K-tile through 4 LDS stages with buffer_load ... lds (global ->
-//    LDS, no VGPRs), 3 K-tiles ahead.  The stream runs across tile boundaries, so the next
-//    tile's first K-tiles load while the current tile finishes and writes its epilogue.
-//    Out-of-range rows read through an out-of-bounds buffer offset, which returns zeros;
-//  * LDS rows are 64 bytes; 16-byte chunk c of row r sits at position c ^ ((r >> 2) & 3).
+//  * K is streamed 128 bytes per K-tile through 2 LDS stages with buffer_load ... lds (global
+//    -> LDS, no VGPRs).  A row's K-tile is one whole 128-byte cache line and one load
+//    instruction moves 8 such lines, so every line is requested from L2 once (64-byte K-tiles
+//    would request each line twice, in consecutive K-tiles).  The stream runs across tile
+//    boundaries, so the next tile's first K-tiles load while the current tile finishes and
+//    writes its epilogue.  Out-of-range rows and the K tail past K read through an
+//    out-of-bounds buffer offset, which returns zeros;
+//  * LDS rows are 128 bytes; 16-byte chunk c of row r sits at position c ^ ((r >> 1) & 7).
 //    ds_read_b128 serves 16 lanes (256 bytes, all 64 banks) per cycle and a fragment read puts
-//    16 consecutive rows on them: 4 rows share a 256-byte window and the XOR spreads the 4
-//    windows' rows over distinct positions, so the reads are bank-conflict free;
-//  * one barrier per K-tile, in its middle: by then the next K-tile has landed (it was issued
-//    two K-tiles earlier) and every wave is past its reads of the stage about to be refilled;
-//    fragments are always read one MFMA sub-step ahead;
+//    16 consecutive rows on them: a row pair shares a 256-byte window and the XOR spreads the 8
+//    pairs over distinct positions, so the reads are bank-conflict free;
+//  * one barrier per K-tile, before its last MFMA sub-step: by then every wave has issued its
+//    reads of this stage (fragments are read one sub-step ahead) and the next K-tile, issued a
+//    whole K-tile earlier, has landed; the stage just read is then refilled with the K-tile
+//    after next;
 //  * the epilogue converts in registers and stores 16 bytes per lane straight to global memory
 //    (lane pairs exchange halves with v_permlane32_swap so each store covers 8 columns); the
 //    tile's sx/sw/bias are loaded into LDS with its first K-tile (4 rotating buffers: with short
@@ -38,15 +42,15 @@
 namespace convrot {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64, NST = 4;
-constexpr int OPB = 256 * BK;                 // bytes of one operand per stage (16 KiB)
+constexpr int BM = 256, BN = 256, BK = 128, NST = 2;
+constexpr int OPB = 256 * BK;                 // bytes of one operand per stage (32 KiB)
 constexpr int STAGE = 2 * OPB;                // weight rows then token rows
 constexpr int SCALE_OFF = NST * STAGE;        // 128 KiB
 constexpr int SCALE_BYTES = 4 * (2 * BN + BM);
 constexpr int NSCALE = 4;
 constexpr int SMEM = SCALE_OFF + NSCALE * SCALE_BYTES;
 constexpr int NTHREADS = 512;
-constexpr int GROUP_M = 16;
+constexpr int GROUP_M = 4;
 constexpr int WG_PER_CU = 1;
 constexpr uint32_t OOB = 0x80000000u;         // buffer offset past num_records -> loads return 0
 constexpr int NUM_RECORDS = 0x7ffffff0;
@@ -65,7 +69,7 @@ struct GemmParams {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n only.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
@@ -93,26 +97,26 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wn = w & 1, wm = w >> 1;   // wn: 128-row half of N, wm: 64-row quarter of M
     const int K = p.K;
-    const int KT = K / BK;
+    const int KT = (K + BK - 1) / BK;          // the last K-tile may be half (K % 128 == 64)
     const int T = p.tiles_m * p.tiles_n;
     // number of tiles of this workgroup: virtual ids blockIdx.x + k*gridDim.x < T
     const int ntiles = (T - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
     const int total = ntiles * KT;            // K-tiles in this workgroup's stream
 
-    // Per-lane load geometry (independent of the tile): instruction i (0..1) of wave w fills
-    // LDS rows 16*(8i+w) .. +15 of an operand stage; lane -> row +lane/4 at 16-byte position
-    // lane%4, which holds K chunk (lane%4) ^ swz(row).
-    int lrow[2], lchunk[2];
+    // Per-lane load geometry (independent of the tile): instruction i (0..3) of wave w fills
+    // LDS rows 8*(8i+w) .. +7 of an operand stage; lane -> row +lane/8 at 16-byte position
+    // lane%8, which holds K chunk (lane%8) ^ swz(row).
+    int lrow[4], lchunk[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        lrow[i] = 16 * (8 * i + w) + (lane >> 2);
-        lchunk[i] = (lane & 3) ^ swz(lrow[i]);
+    for (int i = 0; i < 4; ++i) {
+        lrow[i] = 8 * (8 * i + w) + (lane >> 3);
+        lchunk[i] = (lane & 7) ^ swz(lrow[i]);
     }
 
     // Current load-side tile (the stream runs ahead of the compute-side tile).
     int ld_t = -1, ld_tm = 0, ld_tn = 0;
     __amdgpu_buffer_rsrc_t rw, rx;
-    uint32_t offw[2], offx[2];
+    uint32_t offw[4], offx[4];
     auto set_load_tile = [&](int t) {
         ld_t = t;
         tile_of((int)blockIdx.x + t * (int)gridDim.x, T, p.tiles_m, p.tiles_n, ld_tm, ld_tn);
@@ -120,7 +124,7 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
         rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(p.wq + n0 * K), (short)0, NUM_RECORDS, 0x00020000);
         rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(p.xq + m0 * K), (short)0, NUM_RECORDS, 0x00020000);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const uint32_t o = (uint32_t)(lrow[i] * K + 16 * lchunk[i]);
             offw[i] = n0 + lrow[i] < p.N ? o : OOB;
             offx[i] = m0 + lrow[i] < p.M ? o : OOB;
@@ -149,8 +153,8 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
             }
         }
     };
-    // Issue the loads of the next K-tile of the stream (4 buffer_load ... lds per wave, plus the
-    // scales with a tile's first K-tile) into LDS stage (g & 3).  The load side walks the stream
+    // Issue the loads of the next K-tile of the stream (8 buffer_load ... lds per wave, plus the
+    // scales with a tile's first K-tile) into LDS stage (g & 1).  The load side walks the stream
     // in order: (ld_t, ld_kt) is the K-tile it issues next.
     int ld_kt = 0;
     auto issue = [&](int g) {
@@ -162,19 +166,21 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
         if (++ld_kt == KT) ld_kt = 0;
         uint8_t *base = smem + (g & (NST - 1)) * STAGE + w * 1024;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 4; ++i) {
+            const bool kin = k0 + 16 * lchunk[i] < (uint32_t)K;     // half K-tile at the end of K
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + 8 * i * 1024), 16,
-                                                     offw[i] == OOB ? OOB : offw[i] + k0, 0, 0, 0);
+                                                     (offw[i] == OOB || !kin) ? OOB : offw[i] + k0, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(base + OPB + 8 * i * 1024), 16,
-                                                     offx[i] == OOB ? OOB : offx[i] + k0, 0, 0, 0);
+                                                     (offx[i] == OOB || !kin) ? OOB : offx[i] + k0, 0, 0, 0);
         }
     };
 
     // Fragment addressing: row = wave base + 32*blk + lane%32 (bases are multiples of 32, so
-    // swz(row) == swz(lane%32)); sub-step kk reads K chunk 2*kk + lane/32.
+    // swz(row) == swz(lane%32)); sub-step kk (0..3) reads K chunk 2*kk + lane/32.
     const int frow = lane & 31, fhalf = lane >> 5;
     const int arow = (wn * 128 + frow) * BK, brow = OPB + (wm * 64 + frow) * BK;
-    const int fpos[2] = {((0 + fhalf) ^ swz(frow)) * 16, ((2 + fhalf) ^ swz(frow)) * 16};
+    const int fpos[4] = {((0 + fhalf) ^ swz(frow)) * 16, ((2 + fhalf) ^ swz(frow)) * 16,
+                         ((4 + fhalf) ^ swz(frow)) * 16, ((6 + fhalf) ^ swz(frow)) * 16};
     v4i fa[2][4], fb[2][2];
     auto read_frags = [&](int g, int kk, int buf) {
         const uint8_t *s0 = smem + (g & (NST - 1)) * STAGE + fpos[kk];
@@ -295,14 +301,13 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
     };
 
     if (ntiles <= 0) return;
-    // prologue: K-tiles 0..2 in flight, K-tile 0 (and tile 0's scales) visible, first fragments
+    // Stores each wavefront has in flight after an epilogue (vmcnt counts them too).
+    constexpr int EPI_STORES = E == Epi::Int32 ? 32 : 16;
+    // prologue: K-tile 0 (and tile 0's scales) visible, K-tile 1 in flight, first fragments
     issue(0);
-    if (total > 1) issue(1);
-    if (total > 2) issue(2);
-    if (total > 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
-    else if (total > 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
+    if (total > 1) issue(1);
     read_frags(0, 0, 0);
 
     int g = 0;
@@ -312,17 +317,26 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
             fence();
             mfmas(0);
             fence();
-            // K-tile g+1 must have landed.  Issued after its loads: K-tile g+2's 4 loads and, in
-            // the first two K-tiles of a tile, the previous tile's 16 epilogue stores (vmcnt
-            // counts stores too; they may keep draining).
-            if (g + 2 < total) {
-                if (t > 0 && kt < 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(20));
-                else __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
-            } else {
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            read_frags(g, 2, 0);
+            fence();
+            mfmas(1);
+            fence();
+            read_frags(g, 3, 1);
+            fence();
+            mfmas(0);
+            fence();
+            // K-tile g+1 must have landed before its first fragments are read.  Issued after
+            // its loads: at most the previous tile's epilogue stores, right after an epilogue
+            // (and only with 16-byte stores; otherwise wait for everything).
+            if (g + 1 < total) {
+                if (VEC && t > 0 && kt == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(EPI_STORES));
+                else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             }
-            __syncthreads();
-            if (g + 3 < total) issue(g + 3);
+            // Every wave has completed (lgkmcnt(0)) its reads of stage g & 1 and waited for its
+            // loads of K-tile g+1.  A raw barrier: the fence of __syncthreads() would make the
+            // compiler wait for every store in flight as well.
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (g + 2 < total) issue(g + 2);
             if (g + 1 < total) read_frags(g + 1, 0, 0);
             fence();
             mfmas(1);
