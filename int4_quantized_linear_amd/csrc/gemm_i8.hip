@@ -156,22 +156,35 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
     // Issue the loads of the next K-tile of the stream (8 buffer_load ... lds per wave, plus the
     // scales with a tile's first K-tile) into LDS stage (g & 1).  The load side walks the stream
     // in order: (ld_t, ld_kt) is the K-tile it issues next.
+    // The K position goes in the scalar offset, so a K-tile costs no VALU: an out-of-range row's
+    // lane offset (OOB) stays past num_records with any K added.  Only a half K-tile at the end
+    // of K (K % 128 == 64) needs per-lane offsets, to read zeros for the chunks past K.
     int ld_kt = 0;
+    const bool khalf = (K % BK) != 0;
     auto issue = [&](int g) {
         if (ld_kt == 0) {
             set_load_tile(ld_t + 1);
             issue_scales(ld_t);
         }
-        const uint32_t k0 = (uint32_t)(ld_kt * BK);
+        const int k0 = __builtin_amdgcn_readfirstlane(ld_kt * BK);
+        const bool tail = khalf && ld_kt == KT - 1;
         if (++ld_kt == KT) ld_kt = 0;
         uint8_t *base = smem + (g & (NST - 1)) * STAGE + w * 1024;
+        if (!tail) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool kin = k0 + 16 * lchunk[i] < (uint32_t)K;     // half K-tile at the end of K
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + 8 * i * 1024), 16,
-                                                     (offw[i] == OOB || !kin) ? OOB : offw[i] + k0, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(base + OPB + 8 * i * 1024), 16,
-                                                     (offx[i] == OOB || !kin) ? OOB : offx[i] + k0, 0, 0, 0);
+            for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + 8 * i * 1024), 16, offw[i], k0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(base + OPB + 8 * i * 1024), 16, offx[i], k0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool kin = lchunk[i] < (BK / 2) / 16;              // chunks 0..3 exist
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + 8 * i * 1024), 16,
+                                                         kin ? offw[i] : OOB, k0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(base + OPB + 8 * i * 1024), 16,
+                                                         kin ? offx[i] : OOB, k0, 0, 0);
+            }
         }
     };
 
@@ -194,13 +207,14 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = v16i{};
-    auto mfmas = [&](int buf) {
+    auto mfma_range = [&](int buf, int j0, int j1) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = j0; j < j1; ++j) {
             const int bi = j >> 1, bj = j & 1;
             acc[bi][bj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[buf][bi], fb[buf][bj], acc[bi][bj], 0, 0, 0);
         }
     };
+    auto mfmas = [&](int buf) { mfma_range(buf, 0, 8); };
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
     // Accumulator layout of a 32x32 block (MFMA rows = weight rows n, columns = tokens m):
@@ -336,10 +350,17 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
             // loads of K-tile g+1.  A raw barrier: the fence of __syncthreads() would make the
             // compiler wait for every store in flight as well.
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            // last sub-step: the loads of K-tile g+2 and the first fragments of g+1 are issued
+            // between its MFMAs, so the matrix pipe is fed while they go out
+            mfma_range(1, 0, 2);
+            fence();
             if (g + 2 < total) issue(g + 2);
+            fence();
+            mfma_range(1, 2, 4);
+            fence();
             if (g + 1 < total) read_frags(g + 1, 0, 0);
             fence();
-            mfmas(1);
+            mfma_range(1, 4, 8);
             fence();
         }
         epilogue(t);
