@@ -87,7 +87,9 @@ int convrot_quantize_act(const void *x, int x_dtype, int64_t M, int64_t K, int g
  * Workspace bytes needed by convrot_linear (bits 8) / convrot_linear_w4a4 (bits 4) for this
  * shape; 0 on invalid arguments.  The workspace must be 256-byte aligned.  It is scratch: the
  * library initialises what it needs on the stream, so any contents are fine on entry and it holds
- * nothing useful afterwards.  convrot_gemm_i8_i32 with M <= 16 needs the same bits-8 size.
+ * nothing useful afterwards.  convrot_gemm_i8_i32 with M <= 16 needs the same bits-8 size and
+ * convrot_gemm_i4_i32 the bits-4 size.  The bits-4 workspace holds both operands' codes widened
+ * to one byte each ((M + N) * K bytes) besides the activation codes and scales.
  */
 size_t convrot_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits);
 
@@ -108,6 +110,7 @@ int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_
  * (row, 256-group) with fp16 scales, per-group integer dot products scaled and summed in fp32.
  *   x bf16/fp32 [M, K] quantized into the workspace, or x = NULL and the caller's
  *   xq uint8 [M, K/2] / x_scale fp16 [K/256, M] from convrot_quantize_act(bits = 4).
+ *   The workspace (convrot_workspace_bytes(M, N, K, 4)) is required in both cases.
  *   wq uint8 [N, K/2], w_scale fp16 [K/256, N] from convrot_prepare_weight(bits = 4).
  *   group must be 256, K % 256 == 0, N % 8 == 0.  bias fp32 [N] or NULL; y bf16 [M, N].
  *   w_scale must be 8-byte aligned (the kernel reads 4 scales at a time).
@@ -123,9 +126,12 @@ int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uin
 int convrot_gemm_i8_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K, int32_t *acc,
                         void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* W4A4 integer core without scales: acc int32 [M, N] = sum_k cx[m,k] * cw[n,k] over packed codes. */
+/*
+ * W4A4 integer core without scales: acc int32 [M, N] = sum_k cx[m,k] * cw[n,k] over packed codes
+ * (same kernels as convrot_linear_w4a4; workspace of convrot_workspace_bytes(M, N, K, 4) bytes).
+ */
 int convrot_gemm_i4_i32(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N, int64_t K, int32_t *acc,
-                        hipStream_t stream);
+                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Description of the last non-OK status returned on the calling thread ("" if none). */
 const char *convrot_last_error(void);

@@ -29,7 +29,7 @@ SIGNATURES = {
     "convrot_linear": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, P, SZ, P], I),
     "convrot_linear_w4a4": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, P, SZ, P], I),
     "convrot_gemm_i8_i32": ([P, P, I64, I64, I64, P, P, SZ, P], I),
-    "convrot_gemm_i4_i32": ([P, P, I64, I64, I64, P, P], I),
+    "convrot_gemm_i4_i32": ([P, P, I64, I64, I64, P, P, SZ, P], I),
     "convrot_last_error": ([], ctypes.c_char_p),
     "convrot_status_string": ([I], ctypes.c_char_p),
 }
@@ -175,5 +175,6 @@ def gemm_i4_i32(xq: torch.Tensor, wq: torch.Tensor) -> torch.Tensor:
     M, Kh = xq.shape
     N = wq.shape[0]
     acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
-    _call("convrot_gemm_i4_i32", _ptr(xq), _ptr(wq), M, N, 2 * Kh, _ptr(acc), _stream(xq.device))
+    ws = _workspace(M, N, 2 * Kh, 4, xq.device)
+    _call("convrot_gemm_i4_i32", _ptr(xq), _ptr(wq), M, N, 2 * Kh, _ptr(acc), _ptr(ws), ws.numel(), _stream(xq.device))
     return acc

@@ -76,9 +76,9 @@ int hip_status(hipError_t e, const char *what)
 
 // Workspace layout, each region 256-byte aligned; all of it is scratch (no initial contents):
 //   bits 8: [split-K counters + partial sums if M <= 16][xq int8 M*K][x_scale fp32 M]
-//   bits 4: [xq packed M*K/2][x_scale fp16 (K/256)*M]
+//   bits 4: [xq packed M*K/2][x_scale fp16 (K/256)*M][unpacked codes (M+N)*K]
 struct WsLayout {
-    size_t gemv = 0, xq = 0, xs = 0, total = 0;
+    size_t gemv = 0, xq = 0, xs = 0, unp = 0, total = 0;
     size_t gemv_bytes = 0;
 };
 
@@ -101,6 +101,8 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int bits)
         off += round256((size_t)(M * K / 2));
         L.xs = off;
         off += round256((size_t)(M * (K / 256) * 2));
+        L.unp = off;
+        off += round256(convrot::w4a4_unpacked_bytes(M, N, (int)K));
     }
     L.total = off;
     return L;
@@ -251,7 +253,7 @@ int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uin
         !aligned(w_scale, 8) || !aligned(y, 16) || (bias && !aligned(bias, 4)))
         return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer (w_scale needs 8 bytes)", who);
     const WsLayout L = ws_layout(M, N, K, 4);
-    if (x && (!workspace || workspace_bytes < L.total || !aligned(workspace, 256)))
+    if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
         return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes", who, L.total);
     if (M == 0 || N == 0) return CONVROT_OK;
     if ((rc = check_device())) return rc;
@@ -265,12 +267,12 @@ int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uin
         x_scale = reinterpret_cast<const uint16_t *>(ws + L.xs);
     }
     return hip_status(convrot::launch_gemm_w4a4(xq, wq, x_scale, w_scale, bias, y, convrot::Epi::Bf16, M, N, (int)K,
-                                                stream),
+                                                static_cast<uint8_t *>(workspace) + L.unp, stream),
                       "gemm_w4a4");
 }
 
 int convrot_gemm_i4_i32(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N, int64_t K, int32_t *acc,
-                        hipStream_t stream)
+                        void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     const char *who = "convrot_gemm_i4_i32";
     int rc = check_shape(M, N, K, 256, who);
@@ -279,11 +281,13 @@ int convrot_gemm_i4_i32(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t
     if (M == 0 || N == 0) return CONVROT_OK;
     if (!xq || !wq || !acc) return fail(CONVROT_ERR_NULL, "%s: xq, wq and acc must be non-NULL", who);
     if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(acc, 16)) return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
-    if (M == 0 || N == 0) return CONVROT_OK;
+    const WsLayout L = ws_layout(M, N, K, 4);
+    if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
+        return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes", who, L.total);
     if ((rc = check_device())) return rc;
-    return hip_status(
-        convrot::launch_gemm_w4a4(xq, wq, nullptr, nullptr, nullptr, acc, convrot::Epi::Int32, M, N, (int)K, stream),
-        "gemm_w4a4");
+    return hip_status(convrot::launch_gemm_w4a4(xq, wq, nullptr, nullptr, nullptr, acc, convrot::Epi::Int32, M, N,
+                                                (int)K, static_cast<uint8_t *>(workspace) + L.unp, stream),
+                      "gemm_w4a4");
 }
 
 } // extern "C"

@@ -149,15 +149,19 @@ CASES = [
     ("convrot_linear_w4a4", w4_args(dt=9), "CONVROT_ERR_DTYPE"),
     ("convrot_linear_w4a4", w4_args(sw=C + 2), "CONVROT_ERR_ALIGN"),
     ("convrot_linear_w4a4", w4_args(ws=None), "CONVROT_ERR_WORKSPACE"),
+    # the widened codes live in the workspace even for pre-quantized activations
+    ("convrot_linear_w4a4", w4_args(x=None, xq=A, xs=C, ws=None, wsb=0), "CONVROT_ERR_WORKSPACE"),
     # integer cores
     ("convrot_gemm_i8_i32", (A, B, 32, 256, 96, C, None, 0, None), "CONVROT_ERR_SHAPE"),
     ("convrot_gemm_i8_i32", (None, B, 32, 256, 512, C, None, 0, None), "CONVROT_ERR_NULL"),
     ("convrot_gemm_i8_i32", (A, B, 32, 256, 512, MIS, None, 0, None), "CONVROT_ERR_ALIGN"),
     ("convrot_gemm_i8_i32", (A, B, 12, 1024, 5120, C, None, 0, None), "CONVROT_ERR_WORKSPACE"),
-    ("convrot_gemm_i4_i32", (A, B, 32, 256, 320, C, None), "CONVROT_ERR_SHAPE"),
-    ("convrot_gemm_i4_i32", (A, B, 32, 250, 512, C, None), "CONVROT_ERR_SHAPE"),
-    ("convrot_gemm_i4_i32", (A, None, 32, 256, 512, C, None), "CONVROT_ERR_NULL"),
-    ("convrot_gemm_i4_i32", (A, B + 4, 32, 256, 512, C, None), "CONVROT_ERR_ALIGN"),
+    ("convrot_gemm_i4_i32", (A, B, 32, 256, 320, C, E, 1 << 30, None), "CONVROT_ERR_SHAPE"),
+    ("convrot_gemm_i4_i32", (A, B, 32, 250, 512, C, E, 1 << 30, None), "CONVROT_ERR_SHAPE"),
+    ("convrot_gemm_i4_i32", (A, None, 32, 256, 512, C, E, 1 << 30, None), "CONVROT_ERR_NULL"),
+    ("convrot_gemm_i4_i32", (A, B + 4, 32, 256, 512, C, E, 1 << 30, None), "CONVROT_ERR_ALIGN"),
+    ("convrot_gemm_i4_i32", (A, B, 32, 256, 512, C, None, 0, None), "CONVROT_ERR_WORKSPACE"),
+    ("convrot_gemm_i4_i32", (A, B, 32, 256, 512, C, E, 4096, None), "CONVROT_ERR_WORKSPACE"),
 ]
 
 
