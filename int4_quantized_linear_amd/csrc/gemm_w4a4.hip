@@ -213,7 +213,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
         for (int b = 0; b < 2; ++b) fb[buf][b] = *reinterpret_cast<const v4i *>(s0 + brow + 32 * b * BK);
     };
     v16i iacc[2][2];                         // current group (first written with a zero C)
-    v16f facc[2][2];                         // sum over groups (first written by a group's fold)
+    v16f facc[2][2];                         // sum over groups (zeroed at each tile's start)
     auto mfmas = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -223,14 +223,16 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
     };
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
-    // Fold of block (bi, bj) of group with scale slot gidx: lane holds token m = lane%32 of the
-    // block and weight rows n = 8*(v/4) + 4*(lane/32) + v%4.  (16*16 = 256 is in sx / 256.)
-    auto fold_block = [&](int gidx, bool first, int bi, int bj) {
+    // Fold of block (bi, bj) of group with scale slot gidx into facc (zeroed at the tile's
+    // start; a select between "first" and "accumulate" forms would cost the VALU both):
+    // lane holds token m = lane%32 of the block and weight rows n = 8*(v/4) + 4*(lane/32) + v%4.
+    // (16*16 = 256 is in sx / 256.)
+    auto fold_block = [&](int gidx, int bi, int bj) {
         if constexpr (E == Epi::Int32) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int s = iacc[bi][bj][v] >> 8;       // exact: every product is 256 * cx * cw
-                facc[bi][bj][v] = first ? __int_as_float(s) : __int_as_float(__float_as_int(facc[bi][bj][v]) + s);
+                facc[bi][bj][v] = __int_as_float(__float_as_int(facc[bi][bj][v]) + s);
             }
         } else {
             const uint16_t *sb = reinterpret_cast<const uint16_t *>(smem + SC_OFF + (gidx & (NSC - 1)) * SC_BYTES);
@@ -245,20 +247,18 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = 4 * q + e;
-                    const float c = sxm * sw4[e];
-                    facc[bi][bj][v] = first ? (float)iacc[bi][bj][v] * c
-                                            : __builtin_fmaf((float)iacc[bi][bj][v], c, facc[bi][bj][v]);
+                    facc[bi][bj][v] = __builtin_fmaf((float)iacc[bi][bj][v], sxm * sw4[e], facc[bi][bj][v]);
                 }
             }
         }
     };
     // First sub-step of a group: fold the previous group (if any) block by block, each right
     // before the zero-C MFMA that restarts that block.
-    auto group_start = [&](bool fold, int gidx, bool first) {
+    auto group_start = [&](bool fold, int gidx) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int bi = j >> 1, bj = j & 1;
-            if (fold) fold_block(gidx, first, bi, bj);
+            if (fold) fold_block(gidx, bi, bj);
             iacc[bi][bj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[0][bi], fb[0][bj], v16i{}, 0, 0, 0);
             fence();
         }
@@ -333,7 +333,13 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
         for (int kt = 0; kt < KT; ++kt, ++g) {
             if ((kt & 1) == 0) {
                 // first K-tile of a group: restart the int32 blocks (folding the previous group)
-                group_start(kt > 0, gidx - 1, kt == 2);
+                if (kt == 0) {
+#pragma unroll
+                    for (int a = 0; a < 2; ++a)
+#pragma unroll
+                        for (int b = 0; b < 2; ++b) facc[a][b] = v16f{};
+                }
+                group_start(kt > 0, gidx - 1);
                 fence();
                 read_frags(g, 1, 1);
             } else {
@@ -368,7 +374,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
         }
         // the tile's last group, then its epilogue
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fold_block(gidx - 1, G == 1, j >> 1, j & 1);
+        for (int j = 0; j < 4; ++j) fold_block(gidx - 1, j >> 1, j & 1);
         epilogue(t);
     }
 }
