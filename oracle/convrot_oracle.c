@@ -288,3 +288,32 @@ int oracle_linear_i4(const int8_t *cx, const uint16_t *sx, const int8_t *cw, con
         }
     return ORACLE_OK;
 }
+
+
+/*
+ * W4A8 linear: INT4 weights with one fp16 scale per (row, group) against INT8 activations with
+ * one fp32 scale per token, both rotated by the same grouped Hadamard (the W4A8 variant of the
+ * ConvRot checkpoints, "MiniMax-H3-W4A8-ConvRot" pages: 4-bit weights, 8-bit activations).
+ *   y[m,n] = sx[m] * sum_j sw[n,j] * (sum_{k in group j} qx[m,k] * cw[n,k]) + bias[n]
+ * Each group's dot product is an exact integer; groups are scaled and summed in fp64 in
+ * increasing j.  sw is [N, K/g] (row-major, this file's layout).
+ */
+int oracle_linear_w4a8(const int8_t *qx, const float *sx, const int8_t *cw, const uint16_t *sw, const float *bias,
+                       int64_t M, int64_t N, int64_t K, int g, double *y)
+{
+    if (!qx || !sx || !cw || !sw || !y || M < 0 || N < 0 || K <= 0 || !is_pow2_upto(g, 1 << 15) || K % g)
+        return ORACLE_ERR_ARG;
+    const int64_t G = K / g;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < G; ++j) {
+                int64_t s = 0;
+                for (int i = 0; i < g; ++i) s += (int64_t)qx[m * K + j * g + i] * (int64_t)cw[n * K + j * g + i];
+                acc += (double)s * oracle_f16_to_double(sw[n * G + j]);
+            }
+            y[m * N + n] = acc * (double)sx[m] + (bias ? (double)bias[n] : 0.0);
+        }
+    return ORACLE_OK;
+}

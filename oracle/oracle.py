@@ -64,6 +64,7 @@ def _load():
             "oracle_gemm_i32_pairs": ([P, P, I64, P, P, I64, P], I),
             "oracle_dequant": ([P, P, P, P, I64, I64, P], I),
             "oracle_linear_i4": ([P, P, P, P, P, I64, I64, I64, I, P], I),
+            "oracle_linear_w4a8": ([P, P, P, P, P, I64, I64, I64, I, P], I),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -199,6 +200,20 @@ def linear_i4(cx, sx, cw, sw, bias, g: int) -> np.ndarray:
     return y
 
 
+def linear_w4a8_codes(qx, sx, cw, sw, bias, g: int) -> np.ndarray:
+    """y = sx[m] * sum_j sw[n,j] * (int dot product of group j) + bias[n]; sw is [N, K/g] fp16."""
+    qx = _c(qx, np.int8)
+    cw = _c(cw, np.int8)
+    sx = _c(sx, np.float32)
+    sw = _c(np.asarray(sw, np.float16).view(np.uint16), np.uint16)
+    bias = None if bias is None else _c(bias, np.float32)
+    M, K = qx.shape
+    N = cw.shape[0]
+    y = np.empty((M, N), np.float64)
+    _check(_load().oracle_linear_w4a8(_p(qx), _p(sx), _p(cw), _p(sw), _p(bias), M, N, K, g, _p(y)), "linear_w4a8")
+    return y
+
+
 # ---------------------------------------------------------------------------------------------
 # The method end to end, step by step in the pages' order.
 # ---------------------------------------------------------------------------------------------
@@ -234,3 +249,11 @@ def linear_w4a4(x: np.ndarray, w: np.ndarray, bias: np.ndarray | None, g: int) -
     cx, sx, px = prepare_i4(x, g)
     y = linear_i4(cx, sx, cw, sw, bias, g)
     return dict(cx=cx, sx=sx, px=px, cw=cw, sw=sw, pw=pw, y=y)
+
+
+def linear_w4a8(x: np.ndarray, w: np.ndarray, bias: np.ndarray | None, g: int) -> dict:
+    """ConvRot W4A8 linear: weights rotated and INT4 per group, tokens rotated and INT8 per token."""
+    cw, sw, pw = prepare_i4(w, g)
+    qx, sx = quantize_act_i8(x, g)
+    y = linear_w4a8_codes(qx, sx, cw, sw, bias, g)
+    return dict(qx=qx, sx=sx, cw=cw, sw=sw, pw=pw, y=y)

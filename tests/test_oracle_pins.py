@@ -295,10 +295,55 @@ def test_w4a4_loses_more_than_w8a8(oracle):
     assert e4 / np.abs(exact).max() < 0.2
 
 
+def test_w4a8_integer_core_and_group_scales(oracle):
+    """W4A8 with unit scales is the plain integer product of INT8 tokens and INT4 weights
+    (numpy int64); a per-group weight scale multiplies only that group's integer dot product,
+    and the token scale multiplies the whole row (checked against numpy block products)."""
+    rng = np.random.default_rng(11)
+    g = 256
+    qx = rng.integers(-127, 128, size=(6, 768), dtype=np.int8)
+    cw = rng.integers(-7, 8, size=(10, 768), dtype=np.int8)
+    y = oracle.linear_w4a8_codes(qx, np.ones(6, np.float32), cw, np.ones((10, 3), np.float16), None, g)
+    assert np.array_equal(y, (qx.astype(np.int64) @ cw.astype(np.int64).T).astype(np.float64))
+    sw = np.ones((10, 3), np.float16)
+    sw[:, 1] = 0.25
+    sw[:, 2] = 2.0
+    sx = np.full(6, 0.5, np.float32)
+    y2 = oracle.linear_w4a8_codes(qx, sx, cw, sw, None, g)
+    parts = [qx[:, j * g:(j + 1) * g].astype(np.int64) @ cw[:, j * g:(j + 1) * g].astype(np.int64).T for j in range(3)]
+    assert np.array_equal(y2, 0.5 * (parts[0] + 0.25 * parts[1] + 2.0 * parts[2]))
+    # per-group integer sums stay far inside int32: 256 * 127 * 7
+    assert max(np.abs(p).max() for p in parts) <= g * 127 * 7
+
+
+def test_w4a8_error_sits_between_w8a8_and_w4a4(oracle):
+    """4-bit weights with 8-bit tokens lose more than W8A8 and less than W4A4 on the same data."""
+    x, w = workloads.tiny_inputs()
+    x = x.double().numpy()
+    w = w.double().numpy()
+    exact = x @ w.T
+    err = {name: np.abs(fn(x, w, None, 256)["y"] - exact).max()
+           for name, fn in (("w8a8", oracle.linear_w8a8), ("w4a8", oracle.linear_w4a8), ("w4a4", oracle.linear_w4a4))}
+    assert err["w8a8"] < err["w4a8"] < err["w4a4"], err
+
+
+def test_w4a8_matches_its_definition_on_a_hand_case(oracle):
+    """Brute force on a tiny case: g = 2, two groups, hand-written codes and scales."""
+    qx = np.array([[3, -1, 2, 5]], np.int8)
+    cw = np.array([[1, 2, -3, 4], [-7, 0, 7, 1]], np.int8)
+    sw = np.array([[0.5, 2.0], [1.0, 0.25]], np.float16)
+    sx = np.array([0.125], np.float32)
+    b = np.array([1.0, -2.0], np.float32)
+    # row 0: group 0: 3*1 + (-1)*2 = 1; group 1: 2*(-3) + 5*4 = 14 -> 0.125 * (0.5*1 + 2*14) + 1
+    # row 1: group 0: 3*(-7) + 0 = -21; group 1: 2*7 + 5*1 = 19 -> 0.125 * (-21 + 0.25*19) - 2
+    y = oracle.linear_w4a8_codes(qx, sx, cw, sw, b, 2)
+    assert np.array_equal(y, np.array([[0.125 * (0.5 + 28.0) + 1.0, 0.125 * (-21.0 + 4.75) - 2.0]]))
+
+
 def test_bias_is_added_once(oracle):
     x, w = workloads.tiny_inputs()
     x = x.double().numpy()
     w = w.double().numpy()
     b = np.arange(256, dtype=np.float32) * 0.125
-    for fn in (oracle.linear_w8a8, oracle.linear_w4a4):
+    for fn in (oracle.linear_w8a8, oracle.linear_w4a4, oracle.linear_w4a8):
         assert np.allclose(fn(x, w, b, 256)["y"] - fn(x, w, None, 256)["y"], b[None, :], rtol=0, atol=1e-12)
