@@ -218,12 +218,42 @@ def bench_decode(cr, wl, torch, steps, warmup):
         tg_eager, te_eager = eager(gemv), eager(e2e)
         wbytes = N * K + 4 * N
         gbs = wbytes / (tg * 1e-6) / 1e9
-        out["K%d_N%d" % (K, N)] = dict(weight_bytes=wbytes, gemv_us=tg, e2e_us=te, weight_GBps=gbs,
-                                       frac_hbm=gbs / PEAK_HBM_GBS, gemv_eager_us=tg_eager, e2e_eager_us=te_eager,
-                                       splits=None, timing="hip graph replay of %d launches" % n_calls)
+        row = dict(weight_bytes=wbytes, gemv_us=tg, e2e_us=te, weight_GBps=gbs,
+                   frac_hbm=gbs / PEAK_HBM_GBS, gemv_eager_us=tg_eager, e2e_eager_us=te_eager,
+                   splits=None, timing="hip graph replay of %d launches" % n_calls)
         log("decode K=%d N=%d: GEMV %.2f us (%.0f GB/s, %.0f%% of HBM), e2e %.2f us; eager %.2f / %.2f us" % (
             K, N, tg, gbs, 100 * gbs / PEAK_HBM_GBS, te, tg_eager, te_eager))
         del wqs, wq0
+        torch.cuda.empty_cache()
+
+        # W4A8: the same tokens (INT8) against INT4 group-scaled weights
+        wq40, ws40 = cr.prepare_weight(w.to(dev), 256, 4)
+        wb4 = N * K // 2 + 2 * N * (K // 256)
+        nw4 = ring_count(wb4)
+        w4s = [wq40] + [wq40.clone() for _ in range(nw4 - 1)]
+        wsz4 = cr.workspace_bytes_w4a8(M, N, K)
+        ws4 = torch.empty(max(wsz4, 256), dtype=torch.uint8, device=dev)
+
+        def gemv4(i):
+            cr._call("convrot_linear_w4a8", None, 0, xq.data_ptr(), xsc.data_ptr(), M, N, K, 256,
+                     w4s[i % nw4].data_ptr(), ws40.data_ptr(), None, y.data_ptr(), ws4.data_ptr(), wsz4,
+                     torch.cuda.current_stream(dev).cuda_stream)
+
+        def e2e4(i):
+            cr._call("convrot_linear_w4a8", xd.data_ptr(), cr.CONVROT_DTYPE_BF16, None, None, M, N, K, 256,
+                     w4s[i % nw4].data_ptr(), ws40.data_ptr(), None, y.data_ptr(), ws4.data_ptr(), wsz4,
+                     torch.cuda.current_stream(dev).cuda_stream)
+
+        n4 = max(nw4, 20)
+        t4 = graph_time_us(torch, gemv4, n4, max(steps, 5))
+        t4e = graph_time_us(torch, e2e4, n4, max(steps, 5))
+        gbs4 = wb4 / (t4 * 1e-6) / 1e9
+        row.update(w4a8_weight_bytes=wb4, w4a8_gemv_us=t4, w4a8_e2e_us=t4e, w4a8_weight_GBps=gbs4,
+                   w4a8_frac_hbm=gbs4 / PEAK_HBM_GBS, w4a8_speedup_vs_w8a8=tg / t4)
+        log("decode K=%d N=%d: W4A8 GEMV %.2f us (%.0f GB/s, %.0f%% of HBM), e2e %.2f us, %.2fx the INT8 GEMV" % (
+            K, N, t4, gbs4, 100 * gbs4 / PEAK_HBM_GBS, t4e, tg / t4))
+        out["K%d_N%d" % (K, N)] = row
+        del w4s, wq40
         torch.cuda.empty_cache()
     return out
 

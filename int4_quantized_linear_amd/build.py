@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libconvrot.so")
 ARCH = "gfx950"
 
-SOURCES = ["convrot_abi.hip", "rotate_quant.hip", "gemm_i8.hip", "gemv_i8.hip", "gemm_w4a4.hip"]
+SOURCES = ["convrot_abi.hip", "rotate_quant.hip", "gemm_i8.hip", "gemv_i8.hip", "gemm_w4a4.hip", "gemv_w4a8.hip"]
 
 # Packed-fp32 VALU forms are disabled on purpose: plain fp32 code is emitted instead.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -28,6 +28,8 @@ SIGNATURES = {
     "convrot_workspace_bytes": ([I64, I64, I64, I], SZ),
     "convrot_linear": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, P, SZ, P], I),
     "convrot_linear_w4a4": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, P, SZ, P], I),
+    "convrot_linear_w4a8": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, P, SZ, P], I),
+    "convrot_workspace_bytes_w4a8": ([I64, I64, I64], SZ),
     "convrot_gemm_i8_i32": ([P, P, I64, I64, I64, P, P, SZ, P], I),
     "convrot_gemm_i4_i32": ([P, P, I64, I64, I64, P, P, SZ, P], I),
     "convrot_last_error": ([], ctypes.c_char_p),
@@ -154,6 +156,27 @@ def linear_w4a4(x: torch.Tensor | None, wq: torch.Tensor, w_scale: torch.Tensor,
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ws = _workspace(M, N, K, 4, dev)
     _call("convrot_linear_w4a4", _ptr(x), _dtype_code(x) if x is not None else 0, _ptr(xq), _ptr(x_scale), M, N, K,
+          group, _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y), _ptr(ws), ws.numel(), _stream(dev))
+    return y
+
+
+def workspace_bytes_w4a8(M: int, N: int, K: int) -> int:
+    return int(load().convrot_workspace_bytes_w4a8(M, N, K))
+
+
+def linear_w4a8(x: torch.Tensor | None, wq: torch.Tensor, w_scale: torch.Tensor, bias: torch.Tensor | None = None,
+                group: int = 256, xq: torch.Tensor | None = None, x_scale: torch.Tensor | None = None,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A8 ConvRot linear (at most 16 tokens): packed int4 weights with fp16 group scales
+    (prepare_weight(bits=4)) against int8 tokens (quantize_act(bits=8), or x quantized here)."""
+    _check_dev(x, wq, w_scale, bias, xq, x_scale, out)
+    N, Kh = wq.shape
+    K = 2 * Kh
+    M = x.shape[0] if x is not None else xq.shape[0]
+    dev = wq.device
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(workspace_bytes_w4a8(M, N, K), 256), dtype=torch.uint8, device=dev)
+    _call("convrot_linear_w4a8", _ptr(x), _dtype_code(x) if x is not None else 0, _ptr(xq), _ptr(x_scale), M, N, K,
           group, _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y), _ptr(ws), ws.numel(), _stream(dev))
     return y
 

@@ -108,6 +108,23 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int bits)
     return L;
 }
 
+// W4A8 workspace: [split-K flags + partial sums][xq int8 M*K][x_scale fp32 M] (the last two are
+// used only when the entry point quantizes x itself, but always counted: one size fits both uses).
+WsLayout ws_layout_w4a8(int64_t M, int64_t N, int64_t K)
+{
+    WsLayout L;
+    size_t off = 0;
+    L.gemv = off;
+    L.gemv_bytes = convrot::gemv_w4a8_workspace_bytes(M, N, (int)K);
+    off += round256(L.gemv_bytes);
+    L.xq = off;
+    off += round256((size_t)(M * K));
+    L.xs = off;
+    off += round256((size_t)M * 4);
+    L.total = off;
+    return L;
+}
+
 int quantize_common(const void *x, int dtype, int64_t R, int64_t K, int group, int bits, void *q, void *scale,
                     hipStream_t stream, const char *who)
 {
@@ -269,6 +286,51 @@ int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uin
     return hip_status(convrot::launch_gemm_w4a4(xq, wq, x_scale, w_scale, bias, y, convrot::Epi::Bf16, M, N, (int)K,
                                                 static_cast<uint8_t *>(workspace) + L.unp, stream),
                       "gemm_w4a4");
+}
+
+size_t convrot_workspace_bytes_w4a8(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || M > CONVROT_W4A8_MAX_M || N < 0 || K <= 0 || K % 256 || K > CONVROT_MAX_K) return 0;
+    return ws_layout_w4a8(M, N, K).total;
+}
+
+int convrot_linear_w4a8(const void *x, int x_dtype, const int8_t *xq, const float *x_scale, int64_t M, int64_t N,
+                        int64_t K, int group, const uint8_t *wq, const uint16_t *w_scale, const float *bias, void *y,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const char *who = "convrot_linear_w4a8";
+    int rc = check_shape(M, N, K, group, who);
+    if (rc) return rc;
+    if (group != 256 || K % 256) return fail(CONVROT_ERR_GROUP, "%s: W4A8 needs group 256 and K %% 256 == 0", who);
+    if (M > CONVROT_W4A8_MAX_M)
+        return fail(CONVROT_ERR_SHAPE, "%s: M=%lld tokens; the W4A8 kernel is the decode path (M <= %d)", who,
+                    (long long)M, CONVROT_W4A8_MAX_M);
+    if (M == 0 || N == 0) return CONVROT_OK;
+    if (!wq || !w_scale || !y) return fail(CONVROT_ERR_NULL, "%s: wq, w_scale and y must be non-NULL", who);
+    if (!x && (!xq || !x_scale)) return fail(CONVROT_ERR_NULL, "%s: give x, or both xq and x_scale", who);
+    if (x && x_dtype != CONVROT_DTYPE_F32 && x_dtype != CONVROT_DTYPE_BF16)
+        return fail(CONVROT_ERR_DTYPE, "%s: x_dtype=%d", who, x_dtype);
+    if ((x && !aligned(x, 16)) || (!x && (!aligned(xq, 16) || !aligned(x_scale, 4))) || !aligned(wq, 16) ||
+        !aligned(w_scale, 2) || !aligned(y, 16) || (bias && !aligned(bias, 4)))
+        return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
+    const WsLayout L = ws_layout_w4a8(M, N, K);
+    if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
+        return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes (got %zu)", who, L.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    if ((rc = check_device())) return rc;
+
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    if (x) {
+        int8_t *qx = reinterpret_cast<int8_t *>(ws + L.xq);
+        float *sx = reinterpret_cast<float *>(ws + L.xs);
+        rc = hip_status(convrot::launch_rotate_quant(x, x_dtype == CONVROT_DTYPE_F32, M, (int)K, 8, 8, qx, sx, stream),
+                        "rotate_quant");
+        if (rc) return rc;
+        xq = qx;
+        x_scale = sx;
+    }
+    return hip_status(convrot::launch_gemv_w4a8(xq, x_scale, wq, w_scale, bias, y, M, N, (int)K, ws + L.gemv, stream),
+                      "gemv_w4a8");
 }
 
 int convrot_gemm_i4_i32(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N, int64_t K, int32_t *acc,

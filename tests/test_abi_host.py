@@ -36,8 +36,8 @@ def lib():
 def test_header_declares_the_boundary():
     fns = header_functions()
     for name in ("convrot_prepare_weight", "convrot_quantize_act", "convrot_linear", "convrot_linear_w4a4",
-                 "convrot_workspace_bytes", "convrot_gemm_i8_i32", "convrot_gemm_i4_i32", "convrot_last_error",
-                 "convrot_status_string"):
+                 "convrot_linear_w4a8", "convrot_workspace_bytes", "convrot_workspace_bytes_w4a8",
+                 "convrot_gemm_i8_i32", "convrot_gemm_i4_i32", "convrot_last_error", "convrot_status_string"):
         assert name in fns
     assert set(fns) == set(cr.SIGNATURES), "binding signatures and header disagree"
 
@@ -71,6 +71,16 @@ def test_workspace_bytes(lib):
     for M, K in [(4096, 5376), (3, 512)]:
         b4 = ws(M, 1024, K, 4)
         assert b4 % 256 == 0 and b4 >= M * K // 2 + 2 * M * (K // 256)
+
+
+def test_workspace_bytes_w4a8(lib):
+    ws = lib.convrot_workspace_bytes_w4a8
+    assert ws(17, 256, 512) == 0 and ws(-1, 256, 512) == 0 and ws(4, -1, 512) == 0
+    assert ws(4, 256, 320) == 0 and ws(4, 256, 0) == 0 and ws(4, 256, 131072 + 256) == 0
+    for M, N, K in [(12, 5120, 5120), (12, 25600, 5120), (12, 5120, 25600), (1, 64, 256), (16, 7, 768), (0, 64, 256)]:
+        b = ws(M, N, K)
+        # the INT8 activation codes and scales fit besides whatever the kernel needs
+        assert b % 256 == 0 and b >= M * K + 4 * M and (b > 0 or M == 0), (M, N, K)
 
 
 A = 0x100000          # fake 256-byte aligned device addresses (never dereferenced)
@@ -151,6 +161,20 @@ CASES = [
     ("convrot_linear_w4a4", w4_args(ws=None), "CONVROT_ERR_WORKSPACE"),
     # the widened codes live in the workspace even for pre-quantized activations
     ("convrot_linear_w4a4", w4_args(x=None, xq=A, xs=C, ws=None, wsb=0), "CONVROT_ERR_WORKSPACE"),
+    # W4A8 decode linear
+    ("convrot_linear_w4a8", w4_args(M=17), "CONVROT_ERR_SHAPE"),
+    ("convrot_linear_w4a8", w4_args(M=12, K=100), "CONVROT_ERR_SHAPE"),
+    ("convrot_linear_w4a8", w4_args(M=12, group=128), "CONVROT_ERR_GROUP"),
+    ("convrot_linear_w4a8", w4_args(M=12, K=320, group=64), "CONVROT_ERR_GROUP"),
+    ("convrot_linear_w4a8", w4_args(M=12, wq=None), "CONVROT_ERR_NULL"),
+    ("convrot_linear_w4a8", w4_args(M=12, x=None, xq=A), "CONVROT_ERR_NULL"),
+    ("convrot_linear_w4a8", w4_args(M=12, dt=4), "CONVROT_ERR_DTYPE"),
+    ("convrot_linear_w4a8", w4_args(M=12, sw=C + 1), "CONVROT_ERR_ALIGN"),
+    ("convrot_linear_w4a8", w4_args(M=12, x=None, xq=A, xs=C + 2), "CONVROT_ERR_ALIGN"),
+    ("convrot_linear_w4a8", w4_args(M=12, y=MIS), "CONVROT_ERR_ALIGN"),
+    ("convrot_linear_w4a8", w4_args(M=12, ws=None), "CONVROT_ERR_WORKSPACE"),
+    ("convrot_linear_w4a8", w4_args(M=12, x=None, xq=A, xs=C, wsb=256), "CONVROT_ERR_WORKSPACE"),
+    ("convrot_linear_w4a8", w4_args(M=12, ws=E + 64), "CONVROT_ERR_WORKSPACE"),
     # integer cores
     ("convrot_gemm_i8_i32", (A, B, 32, 256, 96, C, None, 0, None), "CONVROT_ERR_SHAPE"),
     ("convrot_gemm_i8_i32", (None, B, 32, 256, 512, C, None, 0, None), "CONVROT_ERR_NULL"),
@@ -183,6 +207,8 @@ def test_empty_inputs_are_noops(lib):
     assert lib.convrot_linear(None, 1, None, None, 0, 256, 512, 256, None, None, None, None, None, 0, None) == 0
     assert lib.convrot_linear(None, 1, None, None, 16, 0, 512, 256, None, None, None, None, None, 0, None) == 0
     assert lib.convrot_linear_w4a4(None, 1, None, None, 0, 256, 512, 256, None, None, None, None, None, 0, None) == 0
+    assert lib.convrot_linear_w4a8(None, 1, None, None, 0, 256, 512, 256, None, None, None, None, None, 0, None) == 0
+    assert lib.convrot_linear_w4a8(None, 1, None, None, 5, 0, 512, 256, None, None, None, None, None, 0, None) == 0
     assert lib.convrot_gemm_i8_i32(None, None, 0, 256, 512, None, None, 0, None) == 0
 
 

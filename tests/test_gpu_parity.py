@@ -269,3 +269,66 @@ def test_linear_w4a4_parity(cr, M, N, K):
     P.check_y(_x64(y), yown, "y (own codes)", strict_frac=1e-4)
     # ... and against the oracle end to end
     P.check_y(_x64(y), ref["y"], "y (oracle codes)", strict_frac=2e-2)
+
+
+# ------------------------------------------------------------------ W4A8 (decode, M <= 16)
+
+def _w4a8_case(cr, x, w, b, what):
+    xd, wd = x.to(DEV), w.to(DEV)
+    bd = None if b is None else b.to(DEV)
+    wq, ws = cr.prepare_weight(wd, 256, 4)
+    y = cr.linear_w4a8(xd, wq, ws, bd)
+    xq, xs = cr.quantize_act(xd, 256, 8)
+    y2 = cr.linear_w4a8(None, wq, ws, bd, xq=xq, x_scale=xs)
+    torch.cuda.synchronize()
+    bn = None if b is None else b.numpy()
+    ref = orc.linear_w4a8(_x64(x), _x64(w), bn, 256)
+    P.check_codes(_np(xq), ref["qx"], "qx")
+    P.check_scales_f32(_np(xs), ref["sx"], "sx")
+    P.check_scales_f16(_np(ws).T, ref["sw"], "sw16")
+    P.check_codes(orc.unpack_i4(_np(wq)), ref["cw"], "int4 weight codes", rate=1e-3)
+    # exact integer group sums on the GPU's own codes: only fp32 rounding of the scaled sums differs
+    yown = orc.linear_w4a8_codes(_np(xq), _np(xs), orc.unpack_i4(_np(wq)), _np(ws).T, bn, 256)
+    P.check_y(_x64(y), yown, what + " (own codes)", strict_frac=1e-4)
+    P.check_y(_x64(y), ref["y"], what + " (oracle codes)", strict_frac=2e-2)
+    assert torch.equal(y, y2), "pre-quantized path differs from the fused path"
+    return y
+
+
+W4A8_CASES = [
+    # M, N, K: one group (no split), ragged row tiles, several splits, the longest K
+    (5, 64, 256), (1, 200, 512), (16, 520, 768), (12, 1000, 5120), (13, 1024, 5376), (7, 130, 25600),
+    (12, 64, 131072),
+]
+
+
+@pytest.mark.parametrize("M,N,K", W4A8_CASES)
+def test_linear_w4a8_parity(cr, M, N, K):
+    P.say("linear_w4a8 M=%d N=%d K=%d" % (M, N, K))
+    x, w, b = workloads.ragged_case(M, K, N, seed=7)
+    _w4a8_case(cr, x, w, b, "w4a8 y")
+
+
+@pytest.mark.parametrize("K,N", workloads.DECODE_SHAPES)
+def test_linear_w4a8_decode_shapes(cr, K, N):
+    P.say("w4a8 decode M=12 K=%d N=%d" % (K, N))
+    x, w = workloads.decode_inputs(K, N)
+    _w4a8_case(cr, x, w, None, "w4a8 decode y")
+
+
+def test_linear_w4a8_repeat_and_limits(cr):
+    K, N = 5120, 1024
+    w = workloads.gaussian_weights(N, K, cfg=97).to(DEV)
+    wq, ws = cr.prepare_weight(w, 256, 4)
+    y = cr.linear_w4a8(torch.empty(0, K, dtype=torch.bfloat16, device=DEV), wq, ws)
+    assert y.shape == (0, N)
+    # consecutive calls: the caching allocator hands back the same workspace block, whose split-K
+    # flags and partial sums from the previous call must not be taken for this call's
+    for M in (12, 16, 3):
+        x = workloads.heavy_tailed_acts(M, K, cfg=97, layer=M).to(DEV)
+        y = cr.linear_w4a8(x, wq, ws)
+        torch.cuda.synchronize()
+        ref = orc.linear_w4a8(_x64(x), _x64(w), None, 256)
+        P.check_y(_x64(y), ref["y"], "w4a8 repeat M=%d" % M, strict_frac=2e-2)
+    with pytest.raises(cr.ConvRotError, match="M <= 16"):
+        cr.linear_w4a8(torch.zeros(17, K, dtype=torch.bfloat16, device=DEV), wq, ws)
