@@ -226,22 +226,24 @@ def bench_decode(cr, wl, torch, steps, warmup):
         del wqs, wq0
         torch.cuda.empty_cache()
 
-        # W4A8: the same tokens (INT8) against INT4 group-scaled weights
+        # W4A8: the same tokens (INT8) against INT4 group-scaled weights in the W4A8 block layout
         wq40, ws40 = cr.prepare_weight(w.to(dev), 256, 4)
+        wp40 = cr.pack_weight_w4a8(wq40, ws40)
+        del wq40, ws40
         wb4 = N * K // 2 + 2 * N * (K // 256)
         nw4 = ring_count(wb4)
-        w4s = [wq40] + [wq40.clone() for _ in range(nw4 - 1)]
+        w4s = [wp40] + [wp40.clone() for _ in range(nw4 - 1)]
         wsz4 = cr.workspace_bytes_w4a8(M, N, K)
         ws4 = torch.empty(max(wsz4, 256), dtype=torch.uint8, device=dev)
 
         def gemv4(i):
             cr._call("convrot_linear_w4a8", None, 0, xq.data_ptr(), xsc.data_ptr(), M, N, K, 256,
-                     w4s[i % nw4].data_ptr(), ws40.data_ptr(), None, y.data_ptr(), ws4.data_ptr(), wsz4,
+                     w4s[i % nw4].data_ptr(), None, y.data_ptr(), None, 0,
                      torch.cuda.current_stream(dev).cuda_stream)
 
         def e2e4(i):
             cr._call("convrot_linear_w4a8", xd.data_ptr(), cr.CONVROT_DTYPE_BF16, None, None, M, N, K, 256,
-                     w4s[i % nw4].data_ptr(), ws40.data_ptr(), None, y.data_ptr(), ws4.data_ptr(), wsz4,
+                     w4s[i % nw4].data_ptr(), None, y.data_ptr(), ws4.data_ptr(), wsz4,
                      torch.cuda.current_stream(dev).cuda_stream)
 
         n4 = max(nw4, 20)
@@ -253,7 +255,7 @@ def bench_decode(cr, wl, torch, steps, warmup):
         log("decode K=%d N=%d: W4A8 GEMV %.2f us (%.0f GB/s, %.0f%% of HBM), e2e %.2f us, %.2fx the INT8 GEMV" % (
             K, N, t4, gbs4, 100 * gbs4 / PEAK_HBM_GBS, t4e, tg / t4))
         out["K%d_N%d" % (K, N)] = row
-        del w4s, wq40
+        del w4s, wp40
         torch.cuda.empty_cache()
     return out
 

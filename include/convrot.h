@@ -127,19 +127,34 @@ int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uin
  * "MiniMax-H3-W4A8-ConvRot" tutorial page and the news page on MiniMax-H3's experimental W4A8
  * format in ComfyUI describe this format; the nvfp4-convrot page, section 七, says the W4A4
  * kernel takes an INT8-activation path on GPUs without 4-bit tensor-core MMA).  Weights keep the
- * W4A4 format, activations the INT8 one, both rotated by the same grouped Hadamard:
+ * W4A4 quantization, activations the INT8 one, both rotated by the same grouped Hadamard:
  *   y[m,n] = bf16( sx[m] * sum_j sw[j,n] * (sum_{k in group j} qx[m,k] * cw[n,k]) + bias[n] )
  *   x bf16/fp32 [M, K] rotated and quantized to INT8 into the workspace, or x = NULL and the
  *   caller's xq int8 [M, K] / x_scale fp32 [M] from convrot_quantize_act(bits = 8).
- *   wq uint8 [N, K/2], w_scale fp16 [K/256, N] from convrot_prepare_weight(bits = 4).
- *   group must be 256, K % 256 == 0, 0 <= M <= CONVROT_W4A8_MAX_M (CONVROT_ERR_SHAPE otherwise;
- *   larger batches belong on convrot_linear or convrot_linear_w4a4).  bias fp32 [N] or NULL;
- *   y bf16 [M, N].  The workspace (convrot_workspace_bytes_w4a8 bytes, 256-byte aligned) is
- *   required: it holds the split-K partial sums and, with x given, the INT8 activations.
+ *   w_packed: the weights in the W4A8 block layout, from convrot_pack_weight_w4a8.
+ *   group must be 256, K % 256 == 0, N % 8 == 0, 0 <= M <= CONVROT_W4A8_MAX_M
+ *   (CONVROT_ERR_SHAPE otherwise; larger batches belong on convrot_linear or convrot_linear_w4a4).
+ *   bias fp32 [N] or NULL; y bf16 [M, N].  With x given, the workspace
+ *   (convrot_workspace_bytes_w4a8 bytes, 256-byte aligned) holds the INT8 activations; with
+ *   x = NULL none is needed (may be NULL).
  */
 int convrot_linear_w4a8(const void *x, int x_dtype, const int8_t *xq, const float *x_scale, int64_t M, int64_t N,
-                        int64_t K, int group, const uint8_t *wq, const uint16_t *w_scale, const float *bias, void *y,
-                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+                        int64_t K, int group, const void *w_packed, const float *bias, void *y, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Offline re-layout of INT4 weights for convrot_linear_w4a8: wq uint8 [N, K/2] and w_scale fp16
+ * [K/256, N] from convrot_prepare_weight(bits = 4) go into one buffer of
+ * convrot_packed_bytes_w4a8(N, K) bytes (16-byte aligned), ordered the way the decode kernel
+ * streams them: per 64-row tile and 256-channel group, the tile's codes (8 KiB, in MFMA operand
+ * order) followed by its 64 scales; rows past N are zero.  The codes and scales are copied
+ * unchanged (no requantization).  K % 256 == 0.
+ */
+int convrot_pack_weight_w4a8(const uint8_t *wq, const uint16_t *w_scale, int64_t N, int64_t K, void *w_packed,
+                             hipStream_t stream);
+
+/* Size of the W4A8 packed weight buffer; 0 on invalid arguments. */
+size_t convrot_packed_bytes_w4a8(int64_t N, int64_t K);
 
 /* Workspace bytes for convrot_linear_w4a8 at this shape (scratch, like convrot_workspace_bytes);
  * 0 on invalid arguments (M outside [0, CONVROT_W4A8_MAX_M], K not a positive multiple of 256). */

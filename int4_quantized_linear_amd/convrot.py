@@ -28,7 +28,9 @@ SIGNATURES = {
     "convrot_workspace_bytes": ([I64, I64, I64, I], SZ),
     "convrot_linear": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, P, SZ, P], I),
     "convrot_linear_w4a4": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, P, SZ, P], I),
-    "convrot_linear_w4a8": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, P, SZ, P], I),
+    "convrot_linear_w4a8": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, SZ, P], I),
+    "convrot_pack_weight_w4a8": ([P, P, I64, I64, P, P], I),
+    "convrot_packed_bytes_w4a8": ([I64, I64], SZ),
     "convrot_workspace_bytes_w4a8": ([I64, I64, I64], SZ),
     "convrot_gemm_i8_i32": ([P, P, I64, I64, I64, P, P, SZ, P], I),
     "convrot_gemm_i4_i32": ([P, P, I64, I64, I64, P, P, SZ, P], I),
@@ -164,20 +166,35 @@ def workspace_bytes_w4a8(M: int, N: int, K: int) -> int:
     return int(load().convrot_workspace_bytes_w4a8(M, N, K))
 
 
-def linear_w4a8(x: torch.Tensor | None, wq: torch.Tensor, w_scale: torch.Tensor, bias: torch.Tensor | None = None,
-                group: int = 256, xq: torch.Tensor | None = None, x_scale: torch.Tensor | None = None,
-                out: torch.Tensor | None = None) -> torch.Tensor:
-    """W4A8 ConvRot linear (at most 16 tokens): packed int4 weights with fp16 group scales
-    (prepare_weight(bits=4)) against int8 tokens (quantize_act(bits=8), or x quantized here)."""
-    _check_dev(x, wq, w_scale, bias, xq, x_scale, out)
+def packed_bytes_w4a8(N: int, K: int) -> int:
+    return int(load().convrot_packed_bytes_w4a8(N, K))
+
+
+def pack_weight_w4a8(wq: torch.Tensor, w_scale: torch.Tensor) -> torch.Tensor:
+    """Re-lay out INT4 weights (prepare_weight(bits=4): wq uint8 [N, K/2], w_scale fp16 [K/256, N])
+    into the W4A8 decode kernel's block layout (a flat uint8 buffer)."""
+    _check_dev(wq, w_scale)
     N, Kh = wq.shape
     K = 2 * Kh
-    M = x.shape[0] if x is not None else xq.shape[0]
-    dev = wq.device
+    out = torch.empty(max(packed_bytes_w4a8(N, K), 16), dtype=torch.uint8, device=wq.device)
+    _call("convrot_pack_weight_w4a8", _ptr(wq), _ptr(w_scale), N, K, _ptr(out), _stream(wq.device))
+    return out
+
+
+def linear_w4a8(x: torch.Tensor | None, w_packed: torch.Tensor, N: int, bias: torch.Tensor | None = None,
+                group: int = 256, xq: torch.Tensor | None = None, x_scale: torch.Tensor | None = None,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A8 ConvRot linear (at most 16 tokens): INT4 weights in the W4A8 block layout
+    (pack_weight_w4a8) with N output channels, against int8 tokens (quantize_act(bits=8), or x
+    quantized here)."""
+    _check_dev(x, w_packed, bias, xq, x_scale, out)
+    M, K = x.shape if x is not None else xq.shape
+    dev = w_packed.device
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(max(workspace_bytes_w4a8(M, N, K), 256), dtype=torch.uint8, device=dev)
+    # the workspace only holds the quantized tokens when x is given
+    ws = None if x is None else torch.empty(max(workspace_bytes_w4a8(M, N, K), 256), dtype=torch.uint8, device=dev)
     _call("convrot_linear_w4a8", _ptr(x), _dtype_code(x) if x is not None else 0, _ptr(xq), _ptr(x_scale), M, N, K,
-          group, _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y), _ptr(ws), ws.numel(), _stream(dev))
+          group, _ptr(w_packed), _ptr(bias), _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
     return y
 
 

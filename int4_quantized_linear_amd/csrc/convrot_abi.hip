@@ -108,15 +108,11 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int bits)
     return L;
 }
 
-// W4A8 workspace: [split-K flags + partial sums][xq int8 M*K][x_scale fp32 M] (the last two are
-// used only when the entry point quantizes x itself, but always counted: one size fits both uses).
-WsLayout ws_layout_w4a8(int64_t M, int64_t N, int64_t K)
+// W4A8 workspace: [xq int8 M*K][x_scale fp32 M], used when the entry point quantizes x itself.
+WsLayout ws_layout_w4a8(int64_t M, int64_t K)
 {
     WsLayout L;
     size_t off = 0;
-    L.gemv = off;
-    L.gemv_bytes = convrot::gemv_w4a8_workspace_bytes(M, N, (int)K);
-    off += round256(L.gemv_bytes);
     L.xq = off;
     off += round256((size_t)(M * K));
     L.xs = off;
@@ -291,12 +287,34 @@ int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uin
 size_t convrot_workspace_bytes_w4a8(int64_t M, int64_t N, int64_t K)
 {
     if (M < 0 || M > CONVROT_W4A8_MAX_M || N < 0 || K <= 0 || K % 256 || K > CONVROT_MAX_K) return 0;
-    return ws_layout_w4a8(M, N, K).total;
+    return ws_layout_w4a8(M, K).total;
+}
+
+size_t convrot_packed_bytes_w4a8(int64_t N, int64_t K)
+{
+    if (N < 0 || N >= ((int64_t)1 << 31) || K <= 0 || K % 256 || K > CONVROT_MAX_K) return 0;
+    return convrot::w4a8_packed_bytes(N, (int)K);
+}
+
+int convrot_pack_weight_w4a8(const uint8_t *wq, const uint16_t *w_scale, int64_t N, int64_t K, void *w_packed,
+                             hipStream_t stream)
+{
+    const char *who = "convrot_pack_weight_w4a8";
+    int rc = check_shape(N, 1, K, 256, who);
+    if (rc) return rc;
+    if (K % 256) return fail(CONVROT_ERR_GROUP, "%s: K=%lld must be a multiple of 256", who, (long long)K);
+    if (N == 0) return CONVROT_OK;
+    if (!wq || !w_scale || !w_packed) return fail(CONVROT_ERR_NULL, "%s: wq, w_scale and w_packed must be non-NULL", who);
+    if (!aligned(wq, 16) || !aligned(w_scale, 2) || !aligned(w_packed, 16))
+        return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
+    if ((rc = check_device())) return rc;
+    return hip_status(convrot::launch_pack_w4a8(wq, w_scale, N, (int)K, static_cast<uint8_t *>(w_packed), stream),
+                      "pack_w4a8");
 }
 
 int convrot_linear_w4a8(const void *x, int x_dtype, const int8_t *xq, const float *x_scale, int64_t M, int64_t N,
-                        int64_t K, int group, const uint8_t *wq, const uint16_t *w_scale, const float *bias, void *y,
-                        void *workspace, size_t workspace_bytes, hipStream_t stream)
+                        int64_t K, int group, const void *w_packed, const float *bias, void *y, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream)
 {
     const char *who = "convrot_linear_w4a8";
     int rc = check_shape(M, N, K, group, who);
@@ -305,16 +323,17 @@ int convrot_linear_w4a8(const void *x, int x_dtype, const int8_t *xq, const floa
     if (M > CONVROT_W4A8_MAX_M)
         return fail(CONVROT_ERR_SHAPE, "%s: M=%lld tokens; the W4A8 kernel is the decode path (M <= %d)", who,
                     (long long)M, CONVROT_W4A8_MAX_M);
+    if (N % 8) return fail(CONVROT_ERR_SHAPE, "%s: N=%lld must be a multiple of 8", who, (long long)N);
     if (M == 0 || N == 0) return CONVROT_OK;
-    if (!wq || !w_scale || !y) return fail(CONVROT_ERR_NULL, "%s: wq, w_scale and y must be non-NULL", who);
+    if (!w_packed || !y) return fail(CONVROT_ERR_NULL, "%s: w_packed and y must be non-NULL", who);
     if (!x && (!xq || !x_scale)) return fail(CONVROT_ERR_NULL, "%s: give x, or both xq and x_scale", who);
     if (x && x_dtype != CONVROT_DTYPE_F32 && x_dtype != CONVROT_DTYPE_BF16)
         return fail(CONVROT_ERR_DTYPE, "%s: x_dtype=%d", who, x_dtype);
-    if ((x && !aligned(x, 16)) || (!x && (!aligned(xq, 16) || !aligned(x_scale, 4))) || !aligned(wq, 16) ||
-        !aligned(w_scale, 2) || !aligned(y, 16) || (bias && !aligned(bias, 4)))
+    if ((x && !aligned(x, 16)) || (!x && (!aligned(xq, 16) || !aligned(x_scale, 4))) || !aligned(w_packed, 16) ||
+        !aligned(y, 16) || (bias && !aligned(bias, 4)))
         return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
-    const WsLayout L = ws_layout_w4a8(M, N, K);
-    if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
+    const WsLayout L = ws_layout_w4a8(M, K);
+    if (x && (!workspace || workspace_bytes < L.total || !aligned(workspace, 256)))
         return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes (got %zu)", who, L.total,
                     workspace ? workspace_bytes : (size_t)0);
     if ((rc = check_device())) return rc;
@@ -329,7 +348,8 @@ int convrot_linear_w4a8(const void *x, int x_dtype, const int8_t *xq, const floa
         xq = qx;
         x_scale = sx;
     }
-    return hip_status(convrot::launch_gemv_w4a8(xq, x_scale, wq, w_scale, bias, y, M, N, (int)K, ws + L.gemv, stream),
+    return hip_status(convrot::launch_gemv_w4a8(xq, x_scale, static_cast<const uint8_t *>(w_packed), bias, y, M, N,
+                                                (int)K, stream),
                       "gemv_w4a8");
 }
 

@@ -1,285 +1,384 @@
 // gemv_w4a8.hip -- decode-shaped W4A8 ConvRot linear (M <= 16 tokens), weight-bandwidth bound.
 //
-// INT4 weights (one fp16 scale per (row, 256-channel group), two codes per byte) against INT8
-// tokens (one fp32 scale per token), both rotated by the same grouped Hadamard (the W4A8
-// ConvRot variant: 4-bit weights, 8-bit activations, "MiniMax-H3-W4A8-ConvRot" pages):
+// INT4 weights (one fp16 scale per (row, 256-channel group)) against INT8 tokens (one fp32 scale
+// per token), both rotated by the same grouped Hadamard (the W4A8 format of the MiniMax-H3
+// W4A8 ConvRot pages: 4-bit weights, 8-bit activations):
 //   y[m,n] = bf16( sx[m] * sum_j sw[j,n] * (sum_{k in group j} qx[m,k] * cw[n,k]) + bias[n] )
-// Half the weight bytes of the INT8 GEMV for the same shape.
 //
-// Design: a workgroup (4 wavefronts) owns 64 weight rows and a slice of the K groups, streamed
-// one group (256 codes = 128 packed bytes per row) per chunk through NST LDS stages with
-// buffer_load ... lds (one instruction moves 8 rows x 128 bytes).  Wavefront w owns rows
-// 16w .. 16w+15 and all four 64-code K-steps of a chunk, so a group's integer dot products
-// finish inside one wavefront and are scaled right away (no cross-wave reduction):
-//  * A operand (weights): 8 packed bytes per lane (ds_read_b64) widened to 16 int8 codes x16 in
-//    natural order (low nibble = even channel), 5 VALU per packed dword;
-//  * B operand (tokens): 16 int8 codes per lane (ds_read_b128); tokens >= M read zeros;
-//  * v_mfma_i32_16x16x64_i8 per K-step (rows = weight rows, columns = tokens); after the group:
-//    facc += float(iacc) * sw / 16, and the next group's first MFMA starts from zero.
-// LDS swizzles: weight row r keeps 16-byte chunk c at c ^ ((r >> 1) & 7), token row t keeps
-// chunk c at c ^ (t & 15); both make the fragment reads conflict-free.  The group's 16 scales of
-// a wavefront arrive with the chunk by a 2-byte load-to-LDS (one scale per dword).
-// Split-K across workgroups when there are too few row tiles: fp32 partials, per-split
-// generation-tagged arrival flags, the split that sees all flags adds the partials in split
-// order (same protocol as the INT8 GEMV).
-#include <stdlib.h>
-
-#include <atomic>
-#include <chrono>
-
+// Weights are re-laid out once (pack_w4a8_kernel) into the order the kernel consumes them, so
+// every load instruction of the hot loop reads 1 KiB of contiguous memory:
+//   tile t (64 rows) x group j -> one block of BS = 8320 bytes at (t * G + j) * BS:
+//     codes: 8 pieces of 1 KiB, piece (b, i) = row block b (rows 16b..16b+15), half i;
+//            lane l = (r = l % 16, q = l / 16) owns 16 bytes = K-steps 2i and 2i+1 of row
+//            16b + r, each K-step two dwords (dA, dB) over the 16 channels
+//            k = 64 kk + 16 q + s (s = 0..15) of the group: byte u of dA holds channel s = u in
+//            its high nibble and s = 4 + u in its low nibble, dB the same for s = 8+u, 12+u;
+//     scales: 128 bytes, fp16 of row 16b + 4q + v at byte 32q + 8b + 2v (zero for rows >= N).
+//   Rows past N are zero codes with zero scales.
+// With that nibble order one K-step's MFMA operand is
+//   [dA & 0xF0F0F0F0, (dA << 4) & 0xF0F0F0F0, dB & 0xF0F0F0F0, (dB << 4) & 0xF0F0F0F0]
+// = the 16 codes times 16 as int8 in channel order (3 VALU per packed dword).
+//
+// GEMV: a workgroup owns 16 or 32 rows (one or two 16-row blocks of a packed tile) and all of K;
+// its NW wavefronts split K into contiguous runs of whole groups.  Each wavefront streams its run
+// on its own, with no barrier in the main loop: per group it loads its code pieces and scale
+// bytes into a ring of D chunks in registers and the group's 16 token rows into its own LDS ring
+// (load-to-LDS, 1 KiB per instruction; token t keeps 16-byte chunk c at c ^ t, so the fragment
+// reads are conflict-free; tokens >= M arrive as zeros).  Per group it computes the 16x16 blocks
+// with v_mfma_i32_16x16x64_i8 (rows = weights, columns = tokens) and folds them:
+// facc += float(iacc) * sw (iacc is 16x the integer dot product, exact in fp32; the 1/16 goes
+// into the final token scale).  The NW partial results are added once at the end through LDS in
+// wavefront order (deterministic).  There is no cross-workgroup reduction: that needs several
+// trips to the device-coherent level, about a microsecond each, more than a small decode call
+// costs in total.  Small N therefore gets more wavefronts per workgroup rather than split-K
+// workgroups (see plan()).
 #include "device_common.hpp"
 #include "launchers.hpp"
 
 namespace convrot {
 namespace {
 
-constexpr int ROWS = 64;
-constexpr int GC = 256;                  // codes per chunk (= one scale group)
-constexpr int KB = GC / 2;               // packed bytes per row per chunk
-constexpr int NST = 4;
-constexpr int WBYTES = ROWS * KB;        // 8 KiB
-constexpr int XBYTES = 16 * GC;          // 4 KiB
-constexpr int SBYTES = 4 * 256;          // one 256-byte scale block per wavefront
-constexpr int STG = WBYTES + XBYTES + SBYTES;
-constexpr int TARGET_WGS = 256;
-constexpr int MAX_SPLITS = 64;
+constexpr int GS = 256;                  // channels per scale group
+constexpr int RBW = 4;                   // 16-row blocks per tile
+constexpr int RT = 16 * RBW;             // rows per tile
+constexpr int CODE_BYTES = RT * GS / 2;  // 8 KiB
+constexpr int BS = CODE_BYTES + 2 * RT;  // + the tile's 64 fp16 scales
+constexpr int TARGET_WAVES = 640;       // about 2.5 wavefronts per CU in all
+constexpr int MIN_GROUPS = 5;            // per wavefront, to amortise its ramp-up and drain
 constexpr uint32_t OOB = 0x80000000u;
 constexpr int NUM_RECORDS = 0x7ffffff0;
 
-struct W4A8Params {
-    const int8_t *xq;
-    const uint8_t *wq;       // packed [N, K/2]
-    const float *sx;
-    const uint16_t *sw;      // [G, N] fp16
-    const float *bias;
-    uint16_t *y;
-    float *part;             // [splits, M, N]
-    unsigned long long *flag;
-    int64_t N;
-    int M, K, splits;
-    unsigned gen;
-};
-
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
+// ------------------------------------------------------------------ packing
 
-// 8 packed bytes (16 codes, even channel in the low nibble) -> 16 bytes 16*c in channel order.
-__device__ __forceinline__ v4i widen16(uint2 d)
+// One thread per 16-byte code piece or per 8-byte scale quad of a block.
+__global__ void __launch_bounds__(256) pack_w4a8_kernel(const uint8_t *__restrict__ wq, const uint16_t *__restrict__ sw,
+                                                        uint8_t *__restrict__ out, int64_t N, int K, int64_t nblocks)
+{
+    const int G = K / GS;
+    const int Kh = K / 2;
+    const int per_block = CODE_BYTES / 16 + RT / 4;      // 512 pieces + 16 scale quads
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= nblocks * per_block) return;
+    const int64_t blk = idx / per_block;
+    const int piece = (int)(idx % per_block);
+    const int64_t t = blk / G;
+    const int j = (int)(blk % G);
+    uint8_t *dst = out + blk * BS;
+    if (piece < CODE_BYTES / 16) {
+        const int bi = piece >> 6, l = piece & 63;
+        const int b = bi >> 1, i = bi & 1;
+        const int r = l & 15, q = l >> 4;
+        const int64_t row = t * RT + 16 * b + r;
+        uint32_t d[4] = {0u, 0u, 0u, 0u};
+        if (row < N) {
+            const uint8_t *src = wq + row * Kh + (int64_t)j * (GS / 2);
+            for (int h = 0; h < 2; ++h) {                // K-step kk = 2i + h
+                const int kk = 2 * i + h;
+                uint32_t nib[16];
+                for (int s = 0; s < 16; ++s) {
+                    const int k = 64 * kk + 16 * q + s;  // channel within the group
+                    const uint8_t byte = src[k >> 1];
+                    nib[s] = (k & 1) ? (byte >> 4) : (byte & 15u);
+                }
+                uint32_t dA = 0, dB = 0;
+                for (int u = 0; u < 4; ++u) {
+                    dA |= ((nib[u] << 4) | nib[4 + u]) << (8 * u);
+                    dB |= ((nib[8 + u] << 4) | nib[12 + u]) << (8 * u);
+                }
+                d[2 * h] = dA;
+                d[2 * h + 1] = dB;
+            }
+        }
+        uint32_t *o = reinterpret_cast<uint32_t *>(dst + 1024 * bi + 16 * l);
+        for (int u = 0; u < 4; ++u) o[u] = d[u];
+    } else {
+        const int sq = piece - CODE_BYTES / 16;          // 0..15: (q, b)
+        const int q = sq >> 2, b = sq & 3;
+        uint16_t v4[4];
+        for (int v = 0; v < 4; ++v) {
+            const int64_t row = t * RT + 16 * b + 4 * q + v;
+            v4[v] = row < N ? sw[(int64_t)j * N + row] : (uint16_t)0;
+        }
+        uint16_t *o = reinterpret_cast<uint16_t *>(dst + CODE_BYTES + 32 * q + 8 * b);
+        for (int v = 0; v < 4; ++v) o[v] = v4[v];
+    }
+}
+
+// ------------------------------------------------------------------ GEMV
+
+struct W4A8Params {
+    const int8_t *xq;
+    const uint8_t *wp;       // packed blocks
+    const float *sx;
+    const float *bias;
+    uint16_t *y;
+    int64_t N;
+    int M, K;
+};
+
+template <int RB>
+struct Chunk {
+    v4i wa[RB][2];           // code pieces (b0 + b, i)
+    uint32_t sc[2 * RB];     // fp16 scales of rows 16(b0 + b) + 4q + v: half v of dword 2b + v/2
+};
+
+__device__ __forceinline__ v4i widen_step(uint32_t dA, uint32_t dB)
 {
     v4i o;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint32_t p = h ? d.y : d.x;
-        const uint32_t lo = (p << 4) & 0xF0F0F0F0u;    // c0 c2 c4 c6 (x16)
-        const uint32_t hi = p & 0xF0F0F0F0u;           // c1 c3 c5 c7 (x16)
-        o[2 * h] = (int)__builtin_amdgcn_perm(hi, lo, 0x05010400u);       // c0 c1 c2 c3
-        o[2 * h + 1] = (int)__builtin_amdgcn_perm(hi, lo, 0x07030602u);   // c4 c5 c6 c7
-    }
+    o[0] = (int)(dA & 0xF0F0F0F0u);
+    o[1] = (int)((dA << 4) & 0xF0F0F0F0u);
+    o[2] = (int)(dB & 0xF0F0F0F0u);
+    o[3] = (int)((dB << 4) & 0xF0F0F0F0u);
     return o;
 }
 
-__global__ void __launch_bounds__(256, 3) gemv_w4a8_kernel(W4A8Params p)
+// s_waitcnt immediate waiting for vmcnt <= n only (gfx9 encoding)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
+
+constexpr int D = 2;                     // chunks (groups) in flight per wavefront
+constexpr int XSTAGE = 16 * GS;          // one group of 16 token rows (4 KiB)
+constexpr int MAX_NW = 8;                // wavefronts per workgroup
+
+// Workgroup = RB 16-row blocks (rows n0 .. n0 + 16 RB - 1) x all of K; wavefront w takes a
+// contiguous run of groups.  Per group it loads its RB code pieces and the scale bytes into a
+// register ring and the group's 16 token rows into its own LDS ring (load-to-LDS, 1 KiB per
+// instruction, token t keeping 16-byte chunk c at c ^ t; tokens >= M arrive as zeros).
+template <int RB>
+__global__ void __launch_bounds__(64 * MAX_NW) gemv_w4a8_kernel(W4A8Params p)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[NST * STG];
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int LPC = 2 * RB + (RB + 1) / 2 + 4;       // loads per chunk, token loads last
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int tile = blockIdx.x, split = blockIdx.y;
-    const int64_t n0 = (int64_t)tile * ROWS;
+    const int nw = blockDim.x >> 6;
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * RB);
+    const int64_t t64 = n0 / RT;                         // packed 64-row tile
+    const int b0 = (int)(n0 % RT) / 16;                  // first row block inside it
     const int K = p.K;
-    const int G = K / GC;
-    const int g_beg = (int)((int64_t)G * split / p.splits);
-    const int g_end = (int)((int64_t)G * (split + 1) / p.splits);
-    const int nchunks = g_end - g_beg;
+    const int G = K / GS;
+    const int g_beg = G * w / nw;                        // nw <= G: every run has a group
+    const int g_end = G * (w + 1) / nw;
+    const int n = g_end - g_beg;
+    const int r = lane & 15, q = lane >> 4;
+    const int M = p.M;
+    const int m = r;
 
-    // Weights: instruction i (0..1) of wave w fills rows 8*(2w+i) .. +7, lane -> row +lane/8,
-    // 16-byte position lane%8 holding chunk (lane%8) ^ ((row >> 1) & 7).
-    const int Kh = K / 2;
-    const __amdgpu_buffer_rsrc_t rw =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(p.wq + n0 * Kh), (short)0, NUM_RECORDS, 0x00020000);
+    // epilogue operands first, so that their latency hides under the main loop
+    float sxm = 0.0f, bia[RB][4];
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) bia[b][v] = 0.0f;
+    if (w == 0) {
+        sxm = p.sx[m < M ? m : 0] * 0.0625f;
+        if (p.bias) {
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+                const int64_t nb = n0 + 16 * b + 4 * q;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) bia[b][v] = p.bias[nb + v < p.N ? nb + v : 0];
+            }
+        }
+    }
+
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(p.wp + t64 * G * (int64_t)BS), (short)0, NUM_RECORDS, 0x00020000);
     const __amdgpu_buffer_rsrc_t rx =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(p.xq), (short)0, NUM_RECORDS, 0x00020000);
-    uint32_t offw[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r = 8 * (2 * w + i) + (lane >> 3);
-        const int c = (lane & 7) ^ ((r >> 1) & 7);
-        offw[i] = n0 + r < p.N ? (uint32_t)(r * Kh + g_beg * KB + 16 * c) : OOB;
-    }
-    // Tokens: wave w fills token rows 4w .. 4w+3, lane -> token +lane/16, position lane%16
-    // holding chunk (lane%16) ^ token.
-    const int t = 4 * w + (lane >> 4);
-    const uint32_t offx = t < p.M ? (uint32_t)(t * K + g_beg * GC + 16 * ((lane & 15) ^ (t & 15))) : OOB;
-    // Scales of this wave's 16 rows for group j: sw[j*N + n0 + 16w + lane], lanes >= 16 off.
-    const int64_t srow = n0 + 16 * w + lane;
-    const bool sok = lane < 16 && srow < p.N;
+    uint8_t *xs = smem + w * (D * XSTAGE);               // this wavefront's token ring
+    // token load j of a group: tokens 4j + lane/16, position lane%16 holding chunk (lane%16) ^ t
+    const int tx = lane >> 4, px = lane & 15;
 
-    auto issue = [&](int c) {
-        uint8_t *st = smem + (c % NST) * STG;
-        const uint32_t kw = (uint32_t)(c * KB), kx = (uint32_t)(c * GC);
+    // chunk c of this wavefront = group g_beg + c.  Chunks past the run load nothing: bit 31 set
+    // in an offset makes it out of range (zeros, no memory access).  Plain arithmetic rather than
+    // selects, which the compiler would turn into branches around the loads.
+    auto load = [&](Chunk<RB> &ch, int slot, int c) {
+        const uint32_t dead = (uint32_t)(c >= n) << 31;
+        const int g = g_beg + c;
+        const uint32_t blk = (uint32_t)g * (uint32_t)BS;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(st + (2 * w + i) * 1024), 16,
-                                                     offw[i] == OOB ? OOB : offw[i] + kw, 0, 0, 2);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(st + WBYTES + w * 1024), 16,
-                                                 offx == OOB ? OOB : offx + kx, 0, 0, 0);
-        // one fp16 scale per lane, zero-extended into a dword of this wave's scale block
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(p.sw + (int64_t)(g_beg + c) * p.N), (short)0, (int)(2 * p.N), 0x00020000);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(st + WBYTES + XBYTES + w * 256), 2,
-                                                 sok ? (uint32_t)(2 * srow) : OOB, 0, 0, 0);
+        for (int b = 0; b < RB; ++b)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                ch.wa[b][i] = __builtin_bit_cast(
+                    v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                             rw, (blk + 1024 * (2 * (b0 + b) + i) + 16 * lane) | dead, 0, 2));
+        // this lane's scale bytes [32q + 8 b0, + 8 RB) of the tile's 128
+        const uint32_t so = (blk + CODE_BYTES + 32 * q + 8 * b0) | dead;
+        if constexpr (RB == 1) {
+            const v2u v = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rw, so, 0, 0));
+            ch.sc[0] = v[0];
+            ch.sc[1] = v[1];
+        } else {
+#pragma unroll
+            for (int h = 0; h < RB / 2; ++h) {
+                const v4u v = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rw, so + 16 * h, 0, 0));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ch.sc[4 * h + e] = v[e];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = 4 * j + tx;
+            const uint32_t off = (uint32_t)(t * K + g * GS + 16 * (px ^ t)) | dead | ((uint32_t)(t >= M) << 31);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(xs + slot * XSTAGE + 1024 * j), 16, off, 0, 0, 0);
+        }
     };
 
-    // Fragments: A row 16w + lane%16, packed bytes 32kk + 8*(lane/16) = 16-byte chunk
-    // 2kk + (lane/16)/2, half (lane/16)&1; B token lane%16, chunk 4kk + lane/16.
-    const int fr = lane & 15, fq = lane >> 4;
-    const int arow = 16 * w + fr;
-    const int abase = arow * KB + 8 * (fq & 1);
-    const int aswz = (arow >> 1) & 7;
-    const int bbase = WBYTES + fr * GC;
-    float facc[4] = {0.f, 0.f, 0.f, 0.f};
+    float facc[RB][4];
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) facc[b][v] = 0.0f;
 
-    if (nchunks > 0) issue(0);
-    if (nchunks > 1) issue(1);
-    if (nchunks > 2) issue(2);
-    for (int c = 0; c < nchunks; ++c) {
-        if (c + 2 < nchunks) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
-        else if (c + 1 < nchunks) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        // raw barrier: __syncthreads()'s fence would wait for every load in flight
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (c + 3 < nchunks) issue(c + 3);
-        const uint8_t *st = smem + (c % NST) * STG;
-        v4i iacc = v4i{};
+    auto compute = [&](const Chunk<RB> &ch, int slot) {
+        // the token rows of this chunk have landed once at most the next chunk's loads remain
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm((D - 1) * LPC));
+        const uint8_t *xst = xs + slot * XSTAGE + r * GS;
+        v4i iacc[RB];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const int ca = 2 * kk + (fq >> 1);
-            // an ext-vector load keeps its type-based alias info, so the compiler adds no vmcnt(0)
-            // for the loads-to-LDS in flight (the explicit waits above order them)
-            const v2u pv = *reinterpret_cast<const v2u *>(st + abase + 16 * (ca ^ aswz));
-            const uint2 pa = make_uint2(pv[0], pv[1]);
-            const v4i xb = *reinterpret_cast<const v4i *>(st + bbase + 16 * ((4 * kk + fq) ^ fr));
-            iacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen16(pa), xb, iacc, 0, 0, 0);
+            // token r, chunk 4kk + q of the group (16 channels 64kk + 16q ..)
+            const v4i xb = *reinterpret_cast<const v4i *>(xst + 16 * ((4 * kk + q) ^ r));
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+                const v4i &src = ch.wa[b][kk >> 1];
+                const v4i a = widen_step((uint32_t)src[2 * (kk & 1)], (uint32_t)src[2 * (kk & 1) + 1]);
+                iacc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xb, kk ? iacc[b] : v4i{}, 0, 0, 0);
+            }
         }
-        // 16x16 layout: lane holds token lane%16 and rows 4*(lane/16) + v of the wave's 16
-        const v4u s4 = *reinterpret_cast<const v4u *>(st + WBYTES + XBYTES + w * 256 + 16 * fq);
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-            facc[v] = __builtin_fmaf((float)iacc[v], (float)__ushort_as_half((unsigned short)s4[v]) * 0.0625f, facc[v]);
-    }
-
-    const int m = fr;
-    const bool mok = m < p.M;
-    int64_t nn[4];
-    bool ok[4];
+        for (int b = 0; b < RB; ++b)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        nn[v] = n0 + 16 * w + 4 * fq + v;
-        ok[v] = mok && nn[v] < p.N;
-    }
-    auto store = [&](int v, float acc) {
-        const float b = p.bias ? p.bias[nn[v]] : 0.0f;
-        const float yv = __builtin_fmaf(acc, p.sx[m], b);
-        p.y[(int64_t)m * p.N + nn[v]] = (uint16_t)(pack_bf16x2(yv, 0.0f) & 0xffffu);
+            for (int v = 0; v < 4; ++v) {
+                const unsigned short h = (unsigned short)(ch.sc[2 * b + (v >> 1)] >> (16 * (v & 1)));
+                facc[b][v] = __builtin_fmaf((float)iacc[b][v], (float)__ushort_as_half(h), facc[b][v]);
+            }
     };
-    if (p.splits == 1) {
+
+    Chunk<RB> ring[D];
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-            if (ok[v]) store(v, facc[v]);
-        return;
+    for (int j = 0; j < D; ++j) {
+        load(ring[j], j, j);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // whole rounds of D chunks, so that the loop body has no branch (a join would make the
+    // compiler drain every load in flight); chunks past the run are zeros and add nothing
+    for (int c0 = 0; c0 < n; c0 += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            compute(ring[j], j);
+            // the ds_reads of this slot must finish before its refill lands
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            load(ring[j], j, c0 + j + D);
+            // keep this order: hoisting a later chunk's unpacking here would wait for its loads
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
-    // split-K: publish fp32 partials, then the arrival flag; whoever sees every flag finishes
-    // in the (now idle) stage memory: a second LDS object would give the stage reads alias scopes
-    // under which the compiler waits for every load-to-LDS in flight before each read
-    int &last_flag = *reinterpret_cast<int *>(smem);
-    const int64_t MN = (int64_t)p.M * p.N;
+    if (nw > 1) {
+        __syncthreads();                                 // every token ring is idle: reuse the LDS
+        float *red = reinterpret_cast<float *>(smem);    // [nw][RB * 4][64]
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-        if (ok[v])
-            __hip_atomic_store(&p.part[split * MN + (int64_t)m * p.N + nn[v]], facc[v], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (w == 0) {
-        const unsigned long long tag = ((unsigned long long)p.gen << 32) | (unsigned)~p.gen;
-        unsigned long long *fl = p.flag + (int64_t)tile * p.splits;
-        if (lane == 0) __hip_atomic_store(fl + split, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0);
-        const bool seen = lane >= p.splits || lane == split ||
-                          __hip_atomic_load(fl + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
-        const bool all = __builtin_amdgcn_ballot_w64(!seen) == 0;
-        if (all && lane < p.splits) __hip_atomic_store(fl + lane, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (lane == 0) last_flag = all;
+        for (int b = 0; b < RB; ++b)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) red[(w * RB * 4 + 4 * b + v) * 64 + lane] = facc[b][v];
+        __syncthreads();
+        if (w != 0) return;
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float s = red[(4 * b + v) * 64 + lane];
+                for (int ww = 1; ww < nw; ++ww) s += red[(ww * RB * 4 + 4 * b + v) * 64 + lane];
+                facc[b][v] = s;
+            }
     }
-    __syncthreads();
-    if (!last_flag) return;
-    // fp32 partials summed in split order (deterministic)
-    for (int v = 0; v < 4; ++v) {
-        if (!ok[v]) continue;
-        const float *pp = p.part + (int64_t)m * p.N + nn[v];
-        float tot = 0.0f;
-        for (int s0 = 0; s0 < p.splits; s0 += 8) {
-            float vals[8];
+    if (m >= M) return;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                vals[j] = (s0 + j < p.splits) ? __hip_atomic_load(pp + (s0 + j) * MN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                              : 0.0f;
+    for (int b = 0; b < RB; ++b) {
+        const int64_t nb = n0 + 16 * b + 4 * q;
+        if (nb >= p.N) continue;
+        float yv[4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) tot += vals[j];
-        }
-        store(v, tot);
+        for (int v = 0; v < 4; ++v) yv[v] = __builtin_fmaf(facc[b][v], sxm, bia[b][v]);
+        // 4 consecutive bf16 of row m (8 bytes, aligned since N % 8 == 0)
+        v2u o;
+        o[0] = pack_bf16x2(yv[0], yv[1]);
+        o[1] = pack_bf16x2(yv[2], yv[3]);
+        *reinterpret_cast<v2u *>(p.y + (int64_t)m * p.N + nb) = o;
     }
 }
 
-unsigned next_generation()
+struct Plan {
+    int rb, nw;
+    int64_t tiles;
+};
+
+// Rows per workgroup: 32 from N = 4096 on, else 16 (more workgroups for small N; each one
+// re-reads the tokens, so not fewer rows than needed).  Wavefronts per workgroup: about
+// TARGET_WAVES in all, but each with at least MIN_GROUPS groups.  Both measured on the decode
+// shapes (N x K = 8192/1024/25600 x 5120, 5120 x 25600): fewer, longer-running wavefronts beat
+// many short ones, whose prologue and final reduction dominate.
+Plan plan(int64_t N, int K)
 {
-    static std::atomic<unsigned> gen{(unsigned)std::chrono::steady_clock::now().time_since_epoch().count() | 1u};
-    unsigned g = gen.fetch_add(1) + 1;
-    return g ? g : gen.fetch_add(1) + 1;
+    Plan pl;
+    pl.rb = N >= 4096 ? 2 : 1;
+    pl.tiles = (N + 16 * pl.rb - 1) / (16 * pl.rb);
+    int64_t nw = (TARGET_WAVES + pl.tiles - 1) / pl.tiles;
+    const int G = K / GS;
+    if (nw > G / MIN_GROUPS) nw = G / MIN_GROUPS;
+    if (nw > MAX_NW) nw = MAX_NW;
+    pl.nw = nw < 1 ? 1 : (int)nw;
+    return pl;
+}
+
+template <int RB>
+hipError_t launch(const W4A8Params &p, const Plan &pl, hipStream_t stream)
+{
+    const size_t lds = (size_t)pl.nw * D * XSTAGE;
+    hipLaunchKernelGGL((gemv_w4a8_kernel<RB>), dim3((unsigned)pl.tiles), dim3(64 * pl.nw), lds, stream, p);
+    return hipGetLastError();
 }
 
 } // namespace
 
-int gemv_w4a8_splits(int64_t N, int K)
+size_t w4a8_packed_bytes(int64_t N, int K)
 {
-    const int64_t tiles = (N + ROWS - 1) / ROWS;
-    int s = (int)((TARGET_WGS + tiles - 1) / tiles);
-    int smax = K / GC;
-    if (smax > MAX_SPLITS) smax = MAX_SPLITS;
-    if (s > smax) s = smax;
-    return s < 1 ? 1 : s;
+    const int64_t tiles = (N + RT - 1) / RT;
+    return (size_t)(tiles * (K / GS) * BS);
 }
 
-size_t gemv_w4a8_workspace_bytes(int64_t M, int64_t N, int K)
+hipError_t launch_pack_w4a8(const uint8_t *wq, const uint16_t *sw, int64_t N, int K, uint8_t *out, hipStream_t stream)
 {
-    const int64_t tiles = (N + ROWS - 1) / ROWS;
-    const int s = gemv_w4a8_splits(N, K);
-    if (s == 1) return 0;
-    return (size_t)(tiles * s * 8 + (int64_t)s * M * N * 4);
+    const int64_t nblocks = (N + RT - 1) / RT * (K / GS);
+    const int64_t threads = nblocks * (CODE_BYTES / 16 + RT / 4);
+    if (threads == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_w4a8_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, wq, sw, out, N,
+                       K, nblocks);
+    return hipGetLastError();
 }
 
-hipError_t launch_gemv_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const uint16_t *sw, const float *bias,
-                            void *y, int64_t M, int64_t N, int K, void *ws, hipStream_t stream)
+int gemv_w4a8_waves(int64_t N, int K) { return plan(N, K).nw; }
+
+hipError_t launch_gemv_w4a8(const int8_t *xq, const float *sx, const uint8_t *wp, const float *bias, void *y,
+                            int64_t M, int64_t N, int K, hipStream_t stream)
 {
     if (M <= 0 || N <= 0) return hipSuccess;
     W4A8Params p;
     p.xq = xq;
-    p.wq = wq;
+    p.wp = wp;
     p.sx = sx;
-    p.sw = sw;
     p.bias = bias;
     p.y = static_cast<uint16_t *>(y);
     p.N = N;
     p.M = (int)M;
     p.K = K;
-    p.splits = gemv_w4a8_splits(N, K);
-    const int64_t tiles = (N + ROWS - 1) / ROWS;
-    p.flag = static_cast<unsigned long long *>(ws);
-    p.part = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + tiles * p.splits * 8);
-    p.gen = next_generation();
-    hipLaunchKernelGGL(gemv_w4a8_kernel, dim3((unsigned)tiles, (unsigned)p.splits), dim3(256), 0, stream, p);
-    return hipGetLastError();
+    const Plan pl = plan(N, K);
+    if (pl.rb == 2) return launch<2>(p, pl, stream);
+    return launch<1>(p, pl, stream);
 }
 
 } // namespace convrot

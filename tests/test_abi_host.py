@@ -36,7 +36,8 @@ def lib():
 def test_header_declares_the_boundary():
     fns = header_functions()
     for name in ("convrot_prepare_weight", "convrot_quantize_act", "convrot_linear", "convrot_linear_w4a4",
-                 "convrot_linear_w4a8", "convrot_workspace_bytes", "convrot_workspace_bytes_w4a8",
+                 "convrot_linear_w4a8", "convrot_pack_weight_w4a8", "convrot_packed_bytes_w4a8",
+                 "convrot_workspace_bytes", "convrot_workspace_bytes_w4a8",
                  "convrot_gemm_i8_i32", "convrot_gemm_i4_i32", "convrot_last_error", "convrot_status_string"):
         assert name in fns
     assert set(fns) == set(cr.SIGNATURES), "binding signatures and header disagree"
@@ -83,6 +84,15 @@ def test_workspace_bytes_w4a8(lib):
         assert b % 256 == 0 and b >= M * K + 4 * M and (b > 0 or M == 0), (M, N, K)
 
 
+def test_packed_bytes_w4a8(lib):
+    pb = lib.convrot_packed_bytes_w4a8
+    assert pb(-1, 512) == 0 and pb(64, 320) == 0 and pb(64, 0) == 0 and pb(64, 131072 + 256) == 0
+    assert pb(0, 512) == 0
+    # 64-row tiles x 256-channel groups, each 8 KiB of codes + 128 bytes of scales
+    for N, K in [(64, 256), (1, 256), (1024, 5120), (1000, 5376), (5120, 25600)]:
+        assert pb(N, K) == -(-N // 64) * (K // 256) * (8192 + 128), (N, K)
+
+
 A = 0x100000          # fake 256-byte aligned device addresses (never dereferenced)
 B = 0x200000
 C = 0x300000
@@ -98,6 +108,11 @@ def q_args(x=A, dtype=1, R=4, K=512, group=256, bits=8, q=B, s=C):
 def lin_args(x=A, dt=1, xq=None, xs=None, M=32, N=256, K=512, group=256, wq=B, sw=C, bias=None, y=D, ws=E,
              wsb=1 << 30):
     return (x, dt, xq, xs, M, N, K, group, wq, sw, bias, y, ws, wsb, None)
+
+
+def w48_args(x=A, dt=1, xq=None, xs=None, M=12, N=256, K=512, group=256, wp=B, bias=None, y=D, ws=E,
+             wsb=1 << 30):
+    return (x, dt, xq, xs, M, N, K, group, wp, bias, y, ws, wsb, None)
 
 
 def w4_args(x=A, dt=1, xq=None, xs=None, M=32, N=256, K=512, group=256, wq=B, sw=C, bias=None, y=D, ws=E,
@@ -161,20 +176,28 @@ CASES = [
     ("convrot_linear_w4a4", w4_args(ws=None), "CONVROT_ERR_WORKSPACE"),
     # the widened codes live in the workspace even for pre-quantized activations
     ("convrot_linear_w4a4", w4_args(x=None, xq=A, xs=C, ws=None, wsb=0), "CONVROT_ERR_WORKSPACE"),
-    # W4A8 decode linear
-    ("convrot_linear_w4a8", w4_args(M=17), "CONVROT_ERR_SHAPE"),
-    ("convrot_linear_w4a8", w4_args(M=12, K=100), "CONVROT_ERR_SHAPE"),
-    ("convrot_linear_w4a8", w4_args(M=12, group=128), "CONVROT_ERR_GROUP"),
-    ("convrot_linear_w4a8", w4_args(M=12, K=320, group=64), "CONVROT_ERR_GROUP"),
-    ("convrot_linear_w4a8", w4_args(M=12, wq=None), "CONVROT_ERR_NULL"),
-    ("convrot_linear_w4a8", w4_args(M=12, x=None, xq=A), "CONVROT_ERR_NULL"),
-    ("convrot_linear_w4a8", w4_args(M=12, dt=4), "CONVROT_ERR_DTYPE"),
-    ("convrot_linear_w4a8", w4_args(M=12, sw=C + 1), "CONVROT_ERR_ALIGN"),
-    ("convrot_linear_w4a8", w4_args(M=12, x=None, xq=A, xs=C + 2), "CONVROT_ERR_ALIGN"),
-    ("convrot_linear_w4a8", w4_args(M=12, y=MIS), "CONVROT_ERR_ALIGN"),
-    ("convrot_linear_w4a8", w4_args(M=12, ws=None), "CONVROT_ERR_WORKSPACE"),
-    ("convrot_linear_w4a8", w4_args(M=12, x=None, xq=A, xs=C, wsb=256), "CONVROT_ERR_WORKSPACE"),
-    ("convrot_linear_w4a8", w4_args(M=12, ws=E + 64), "CONVROT_ERR_WORKSPACE"),
+    # W4A8 decode linear and its weight re-layout
+    ("convrot_linear_w4a8", w48_args(M=17), "CONVROT_ERR_SHAPE"),
+    ("convrot_linear_w4a8", w48_args(K=100), "CONVROT_ERR_SHAPE"),
+    ("convrot_linear_w4a8", w48_args(group=128), "CONVROT_ERR_GROUP"),
+    ("convrot_linear_w4a8", w48_args(K=320, group=64), "CONVROT_ERR_GROUP"),
+    ("convrot_linear_w4a8", w48_args(wp=None), "CONVROT_ERR_NULL"),
+    ("convrot_linear_w4a8", w48_args(x=None, xq=A), "CONVROT_ERR_NULL"),
+    ("convrot_linear_w4a8", w48_args(dt=4), "CONVROT_ERR_DTYPE"),
+    ("convrot_linear_w4a8", w48_args(N=252), "CONVROT_ERR_SHAPE"),
+    ("convrot_linear_w4a8", w48_args(wp=B + 8), "CONVROT_ERR_ALIGN"),
+    ("convrot_linear_w4a8", w48_args(x=None, xq=A, xs=C + 2), "CONVROT_ERR_ALIGN"),
+    ("convrot_linear_w4a8", w48_args(y=MIS), "CONVROT_ERR_ALIGN"),
+    ("convrot_linear_w4a8", w48_args(ws=None), "CONVROT_ERR_WORKSPACE"),
+    ("convrot_linear_w4a8", w48_args(wsb=256), "CONVROT_ERR_WORKSPACE"),
+    ("convrot_linear_w4a8", w48_args(ws=E + 64), "CONVROT_ERR_WORKSPACE"),
+    ("convrot_pack_weight_w4a8", (A, C, 64, 320, B, None), "CONVROT_ERR_SHAPE"),
+    ("convrot_pack_weight_w4a8", (A, C, 64, 100, B, None), "CONVROT_ERR_SHAPE"),
+    ("convrot_pack_weight_w4a8", (A, C, -1, 512, B, None), "CONVROT_ERR_SHAPE"),
+    ("convrot_pack_weight_w4a8", (None, C, 64, 512, B, None), "CONVROT_ERR_NULL"),
+    ("convrot_pack_weight_w4a8", (A, C, 64, 512, None, None), "CONVROT_ERR_NULL"),
+    ("convrot_pack_weight_w4a8", (A, C + 1, 64, 512, B, None), "CONVROT_ERR_ALIGN"),
+    ("convrot_pack_weight_w4a8", (A, C, 64, 512, B + 8, None), "CONVROT_ERR_ALIGN"),
     # integer cores
     ("convrot_gemm_i8_i32", (A, B, 32, 256, 96, C, None, 0, None), "CONVROT_ERR_SHAPE"),
     ("convrot_gemm_i8_i32", (None, B, 32, 256, 512, C, None, 0, None), "CONVROT_ERR_NULL"),
@@ -207,8 +230,9 @@ def test_empty_inputs_are_noops(lib):
     assert lib.convrot_linear(None, 1, None, None, 0, 256, 512, 256, None, None, None, None, None, 0, None) == 0
     assert lib.convrot_linear(None, 1, None, None, 16, 0, 512, 256, None, None, None, None, None, 0, None) == 0
     assert lib.convrot_linear_w4a4(None, 1, None, None, 0, 256, 512, 256, None, None, None, None, None, 0, None) == 0
-    assert lib.convrot_linear_w4a8(None, 1, None, None, 0, 256, 512, 256, None, None, None, None, None, 0, None) == 0
-    assert lib.convrot_linear_w4a8(None, 1, None, None, 5, 0, 512, 256, None, None, None, None, None, 0, None) == 0
+    assert lib.convrot_linear_w4a8(None, 1, None, None, 0, 256, 512, 256, None, None, None, None, 0, None) == 0
+    assert lib.convrot_linear_w4a8(None, 1, None, None, 5, 0, 512, 256, None, None, None, None, 0, None) == 0
+    assert lib.convrot_pack_weight_w4a8(None, None, 0, 512, None, None) == 0
     assert lib.convrot_gemm_i8_i32(None, None, 0, 256, 512, None, None, 0, None) == 0
 
 

@@ -276,10 +276,12 @@ def test_linear_w4a4_parity(cr, M, N, K):
 def _w4a8_case(cr, x, w, b, what):
     xd, wd = x.to(DEV), w.to(DEV)
     bd = None if b is None else b.to(DEV)
+    N = w.shape[0]
     wq, ws = cr.prepare_weight(wd, 256, 4)
-    y = cr.linear_w4a8(xd, wq, ws, bd)
+    wp = cr.pack_weight_w4a8(wq, ws)
+    y = cr.linear_w4a8(xd, wp, N, bd)
     xq, xs = cr.quantize_act(xd, 256, 8)
-    y2 = cr.linear_w4a8(None, wq, ws, bd, xq=xq, x_scale=xs)
+    y2 = cr.linear_w4a8(None, wp, N, bd, xq=xq, x_scale=xs)
     torch.cuda.synchronize()
     bn = None if b is None else b.numpy()
     ref = orc.linear_w4a8(_x64(x), _x64(w), bn, 256)
@@ -297,8 +299,8 @@ def _w4a8_case(cr, x, w, b, what):
 
 W4A8_CASES = [
     # M, N, K: one group (no split), ragged row tiles, several splits, the longest K
-    (5, 64, 256), (1, 200, 512), (16, 520, 768), (12, 1000, 5120), (13, 1024, 5376), (7, 130, 25600),
-    (12, 64, 131072),
+    (5, 64, 256), (1, 200, 512), (16, 520, 768), (12, 1000, 5120), (13, 1024, 5376), (7, 136, 25600),
+    (12, 64, 131072), (3, 8, 512),
 ]
 
 
@@ -316,19 +318,121 @@ def test_linear_w4a8_decode_shapes(cr, K, N):
     _w4a8_case(cr, x, w, None, "w4a8 decode y")
 
 
+def _unpack_w4a8_layout(buf: np.ndarray, N: int, K: int):
+    """CPU reading of the W4A8 block layout as the header and kernel source describe it:
+    per 64-row tile t and group j a block of 8320 bytes at (t*G + j)*8320; piece (b, i) at
+    1024*(2b+i), lane l = (r, q) at 16*l holds K-steps 2i, 2i+1 of row 16b+r as dwords (dA, dB);
+    dA byte u = channel 64kk+16q+u (high nibble) | channel 64kk+16q+4+u (low nibble), dB the
+    same for +8, +12; scales at 8192 + 32q + 8b + 2v for row 16b+4q+v."""
+    G = K // 256
+    T = -(-N // 64)
+    blocks = buf[: T * G * 8320].reshape(T, G, 8320)
+    codes = np.zeros((T * 64, K), np.int8)
+    scales = np.zeros((T * 64, G), np.uint16)
+    def s4(x):
+        return ((x.astype(np.int16) ^ 8) - 8).astype(np.int8)
+    for b in range(4):
+        for i in range(2):
+            piece = blocks[:, :, 1024 * (2 * b + i): 1024 * (2 * b + i + 1)].reshape(T, G, 4, 16, 16)  # q, r, bytes
+            for h in range(2):
+                kk = 2 * i + h
+                for part in range(2):                     # dA (s 0..7), dB (s 8..15)
+                    by = piece[:, :, :, :, 8 * h + 4 * part: 8 * h + 4 * part + 4]    # [T, G, q, r, u]
+                    for u in range(4):
+                        hi, lo = s4(by[..., u] >> 4), s4(by[..., u] & 15)
+                        for q in range(4):
+                            k_hi = 64 * kk + 16 * q + 8 * part + u
+                            for j in range(G):
+                                rows = np.arange(T)[:, None] * 64 + 16 * b + np.arange(16)[None, :]
+                                codes[rows, 256 * j + k_hi] = hi[:, j, q, :]
+                                codes[rows, 256 * j + k_hi + 4] = lo[:, j, q, :]
+    sc = blocks[:, :, 8192:].reshape(T, G, 4, 4, 4, 2)        # q, b, v, 2 bytes
+    sv = sc[..., 0].astype(np.uint16) | (sc[..., 1].astype(np.uint16) << 8)
+    for q in range(4):
+        for b in range(4):
+            for v in range(4):
+                scales[np.arange(T) * 64 + 16 * b + 4 * q + v, :] = sv[:, :, q, b, v]
+    return codes, scales
+
+
+@pytest.mark.parametrize("N,K", [(64, 256), (200, 512), (1024, 5120)])
+def test_pack_w4a8_layout(cr, N, K):
+    """The packed buffer holds exactly the prepared codes and scales, in the documented order,
+    with zero rows past N."""
+    w = workloads.gaussian_weights(N, K, cfg=96).to(DEV)
+    wq, ws = cr.prepare_weight(w, 256, 4)
+    wp = cr.pack_weight_w4a8(wq, ws)
+    torch.cuda.synchronize()
+    assert wp.numel() == cr.packed_bytes_w4a8(N, K)
+    codes, scales = _unpack_w4a8_layout(_np(wp), N, K)
+    assert np.array_equal(codes[:N], orc.unpack_i4(_np(wq)))
+    assert not codes[N:].any() and not scales[N:].any()
+    assert np.array_equal(scales[:N], _np(ws).view(np.uint16).T)
+
+
 def test_linear_w4a8_repeat_and_limits(cr):
     K, N = 5120, 1024
     w = workloads.gaussian_weights(N, K, cfg=97).to(DEV)
     wq, ws = cr.prepare_weight(w, 256, 4)
-    y = cr.linear_w4a8(torch.empty(0, K, dtype=torch.bfloat16, device=DEV), wq, ws)
+    wp = cr.pack_weight_w4a8(wq, ws)
+    y = cr.linear_w4a8(torch.empty(0, K, dtype=torch.bfloat16, device=DEV), wp, N)
     assert y.shape == (0, N)
-    # consecutive calls: the caching allocator hands back the same workspace block, whose split-K
-    # flags and partial sums from the previous call must not be taken for this call's
+    # consecutive calls with different token counts on the same weights
     for M in (12, 16, 3):
         x = workloads.heavy_tailed_acts(M, K, cfg=97, layer=M).to(DEV)
-        y = cr.linear_w4a8(x, wq, ws)
+        y = cr.linear_w4a8(x, wp, N)
         torch.cuda.synchronize()
         ref = orc.linear_w4a8(_x64(x), _x64(w), None, 256)
         P.check_y(_x64(y), ref["y"], "w4a8 repeat M=%d" % M, strict_frac=2e-2)
     with pytest.raises(cr.ConvRotError, match="M <= 16"):
-        cr.linear_w4a8(torch.zeros(17, K, dtype=torch.bfloat16, device=DEV), wq, ws)
+        cr.linear_w4a8(torch.zeros(17, K, dtype=torch.bfloat16, device=DEV), wp, N)
+    # pre-quantized tokens need no workspace at all
+    x = workloads.heavy_tailed_acts(12, K, cfg=97, layer=5).to(DEV)
+    xq, xs = cr.quantize_act(x, 256, 8)
+    y = torch.empty((12, N), dtype=torch.bfloat16, device=DEV)
+    st = torch.cuda.current_stream().cuda_stream
+    cr._call("convrot_linear_w4a8", None, 0, xq.data_ptr(), xs.data_ptr(), 12, N, K, 256, wp.data_ptr(),
+             None, y.data_ptr(), None, 0, st)
+    torch.cuda.synchronize()
+    assert torch.equal(y, cr.linear_w4a8(x, wp, N))
+
+
+# ------------------------------------------------------------------ streams and graph replay
+
+def _replay_matches(fn, out, ref, replays=3):
+    """Capture fn() on a side stream, replay it several times with eager work and
+    synchronisations in between, and check every replay against the eager result."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fn()
+    torch.cuda.synchronize()
+    for i in range(replays):
+        out.zero_()
+        torch.randn(1024, device=DEV).sum()            # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), "replay %d differs from the eager result" % i
+
+
+def test_decode_linears_run_on_the_callers_stream_and_replay(cr):
+    """Every launch goes to the stream the caller passes: the captured graph holds the kernels
+    (a launch on another stream would leave it empty and the output untouched)."""
+    K, N, M = 5120, 1024, 12
+    w = workloads.gaussian_weights(N, K, cfg=95).to(DEV)
+    x = workloads.heavy_tailed_acts(M, K, cfg=95, layer=0).to(DEV)
+    xq, xs = cr.quantize_act(x, 256, 8)
+    wq8, ws8 = cr.prepare_weight(w, 256, 8)
+    wq4, ws4 = cr.prepare_weight(w, 256, 4)
+    wp = cr.pack_weight_w4a8(wq4, ws4)
+    torch.cuda.synchronize()
+    y8 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    y4 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    ref8 = cr.linear(None, wq8, ws8, xq=xq, x_scale=xs).clone()
+    ref4 = cr.linear_w4a8(None, wp, N, xq=xq, x_scale=xs).clone()
+    torch.cuda.synchronize()
+    _replay_matches(lambda: cr.linear(None, wq8, ws8, xq=xq, x_scale=xs, out=y8), y8, ref8)
+    _replay_matches(lambda: cr.linear_w4a8(None, wp, N, xq=xq, x_scale=xs, out=y4), y4, ref4)
