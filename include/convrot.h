@@ -174,6 +174,16 @@ int convrot_gemm_i8_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N
 int convrot_gemm_i4_i32(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N, int64_t K, int32_t *acc,
                         void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Rotation group for a layer under the converter's dynamic mode: the largest group compatible
+ * with the layer, capped by the configured size ("minimax-h3-nvfp4-convrot核心原理", section 四,
+ * detail 3: --dynamic-convrot with --convrot-group-size 256).  Returns the largest power of two
+ * <= max_group dividing K (256 for K = 5120 or 5376, 128 for the K = 2688 adaln projection), or
+ * 0 when K <= 0 or max_group is not a power of two in [1, 256].  Pass the result as `group` to
+ * convrot_prepare_weight, convrot_quantize_act and convrot_linear (the INT4 paths need 256).
+ */
+int convrot_dynamic_group(int64_t K, int max_group);
+
 /* Description of the last non-OK status returned on the calling thread ("" if none). */
 const char *convrot_last_error(void);
 

@@ -34,6 +34,7 @@ SIGNATURES = {
     "convrot_workspace_bytes_w4a8": ([I64, I64, I64], SZ),
     "convrot_gemm_i8_i32": ([P, P, I64, I64, I64, P, P, SZ, P], I),
     "convrot_gemm_i4_i32": ([P, P, I64, I64, I64, P, P, SZ, P], I),
+    "convrot_dynamic_group": ([I64, I], I),
     "convrot_last_error": ([], ctypes.c_char_p),
     "convrot_status_string": ([I], ctypes.c_char_p),
 }
@@ -96,6 +97,14 @@ def _check_dev(*ts):
                 raise ValueError("ConvRot tensors must be on a GPU device")
             if not t.is_contiguous():
                 raise ValueError("ConvRot tensors must be contiguous")
+
+
+def dynamic_group(K: int, max_group: int = 256) -> int:
+    """Largest power-of-two rotation group <= max_group dividing K (dynamic ConvRot mode)."""
+    g = int(load().convrot_dynamic_group(K, max_group))
+    if g == 0:
+        raise ConvRotError(3, "CONVROT_ERR_GROUP: invalid K=%d or max_group=%d" % (K, max_group))
+    return g
 
 
 def workspace_bytes(M: int, N: int, K: int, bits: int = 8) -> int:

@@ -165,6 +165,14 @@ const char *convrot_status_string(int s)
 
 const char *convrot_last_error(void) { return g_last_error.c_str(); }
 
+int convrot_dynamic_group(int64_t K, int max_group)
+{
+    if (K <= 0 || !pow2_group(max_group)) return 0;
+    int g = max_group;
+    while (K % g) g >>= 1;
+    return g;
+}
+
 int convrot_prepare_weight(const void *w, int w_dtype, int64_t N, int64_t K, int group, int bits, void *wq,
                            void *w_scale, hipStream_t stream)
 {

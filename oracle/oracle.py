@@ -95,6 +95,21 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
+def dynamic_group(K: int, max_group: int = 256) -> int:
+    """Rotation group chosen per layer by the converter's dynamic mode: the largest group size
+    compatible with the layer, capped by the configured group size ("minimax-h3-nvfp4-convrot
+    核心原理", section 四, detail 3: --dynamic-convrot picks each layer's largest compatible group,
+    with --convrot-group-size 256).  Reading: compatible = a power of two (a Sylvester Hadamard
+    block) that divides in_features K.  Walks down from max_group, halving, as the definition
+    reads."""
+    if K <= 0 or max_group < 1 or max_group & (max_group - 1):
+        raise ValueError("K must be positive and max_group a power of two")
+    g = max_group
+    while K % g:
+        g //= 2
+    return g
+
+
 def hadamard_entry(i: int, j: int) -> int:
     return int(_load().oracle_hadamard_entry(i, j))
 

@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
     for name in ("convrot_prepare_weight", "convrot_quantize_act", "convrot_linear", "convrot_linear_w4a4",
                  "convrot_linear_w4a8", "convrot_pack_weight_w4a8", "convrot_packed_bytes_w4a8",
                  "convrot_workspace_bytes", "convrot_workspace_bytes_w4a8",
-                 "convrot_gemm_i8_i32", "convrot_gemm_i4_i32", "convrot_last_error", "convrot_status_string"):
+                 "convrot_gemm_i8_i32", "convrot_gemm_i4_i32", "convrot_dynamic_group", "convrot_last_error",
+                 "convrot_status_string"):
         assert name in fns
     assert set(fns) == set(cr.SIGNATURES), "binding signatures and header disagree"
 
@@ -82,6 +83,18 @@ def test_workspace_bytes_w4a8(lib):
         b = ws(M, N, K)
         # the INT8 activation codes and scales fit besides whatever the kernel needs
         assert b % 256 == 0 and b >= M * K + 4 * M and (b > 0 or M == 0), (M, N, K)
+
+
+def test_dynamic_group_matches_the_oracle(lib):
+    from oracle import oracle as orc
+    for K in list(range(1, 1100)) + [2688, 5120, 5376, 25600, 131072]:
+        for mg in (256, 128, 1):
+            assert lib.convrot_dynamic_group(K, mg) == orc.dynamic_group(K, mg), (K, mg)
+    assert lib.convrot_dynamic_group(0, 256) == 0 and lib.convrot_dynamic_group(-5, 256) == 0
+    assert lib.convrot_dynamic_group(512, 96) == 0 and lib.convrot_dynamic_group(512, 512) == 0
+    assert cr.dynamic_group(2688) == 128
+    with pytest.raises(cr.ConvRotError):
+        cr.dynamic_group(512, 3)
 
 
 def test_packed_bytes_w4a8(lib):

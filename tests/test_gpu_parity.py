@@ -175,6 +175,22 @@ def test_linear_decode_shapes(cr, K, N):
     _linear_case(cr, x, w, None, 256)
 
 
+def test_linear_dynamic_group_adaln_width(cr):
+    """A layer whose in_features (2688, the adaln projection's) 256 does not divide: the dynamic
+    group (128) through prepare / quantize / linear, against the oracle at the same group."""
+    K = 2688
+    g = cr.dynamic_group(K)
+    assert g == 128
+    for M, N in [(12, 1000), (300, 2048)]:
+        P.say("dynamic-group linear M=%d N=%d K=%d g=%d" % (M, N, K, g))
+        x, w, b = workloads.ragged_case(M, K, N, seed=11)
+        _linear_case(cr, x, w, b, g)
+    # the INT4 paths keep their 256-channel scale groups: rejected, not silently regrouped
+    w4 = workloads.gaussian_weights(64, K, cfg=94).to(DEV)
+    with pytest.raises(cr.ConvRotError, match="GROUP"):
+        cr.prepare_weight(w4, g, 4)
+
+
 def test_linear_prefill_full_size_sampled(cr):
     """Full 4096 x 5376 x 16128 workload; oracle on 384 sampled token rows / weight rows and
     4096 sampled outputs."""

@@ -347,3 +347,28 @@ def test_bias_is_added_once(oracle):
     b = np.arange(256, dtype=np.float32) * 0.125
     for fn in (oracle.linear_w8a8, oracle.linear_w4a4, oracle.linear_w4a8):
         assert np.allclose(fn(x, w, b, 256)["y"] - fn(x, w, None, 256)["y"], b[None, :], rtol=0, atol=1e-12)
+
+
+def test_dynamic_group_pins(oracle):
+    """Dynamic group choice: the pages' qkv layers (in_features 5376) keep 256 (nvfp4-convrot
+    page, section 四, detail 3), the adaln projection weight [96768, 2688] of the pruning section
+    (2688 = 2^7 * 21) gets 128; the Qwen3 widths keep 256."""
+    assert oracle.dynamic_group(5376) == 256
+    assert oracle.dynamic_group(2688) == 128
+    for K in (5120, 8192, 25600):
+        assert oracle.dynamic_group(K) == 256
+    assert oracle.dynamic_group(2688, 64) == 64
+    assert oracle.dynamic_group(96) == 32 and oracle.dynamic_group(7) == 1
+
+
+def test_dynamic_group_brute_force(oracle):
+    """Against an independent reading of the rule (largest power of two <= 256 among K's
+    divisors, found by listing them) for every K up to 3000."""
+    for K in range(1, 3001):
+        divisors = [d for d in range(1, K + 1) if K % d == 0]
+        best = max(d for d in divisors if d <= 256 and d & (d - 1) == 0)
+        assert oracle.dynamic_group(K) == best, K
+    with pytest.raises(ValueError):
+        oracle.dynamic_group(0)
+    with pytest.raises(ValueError):
+        oracle.dynamic_group(512, 96)
