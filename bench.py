@@ -8,9 +8,10 @@ Inputs and weights cycle through rings of distinct buffers (>= 1 GiB each), so e
 reads HBM rather than the last-level cache.  `value` is whole-step int8 TOP/s.
 
 The same run also measures, each with its own timed loop:
-  * decode (M=12) linears on the four Qwen3-VL-32B-like shapes: weight GB/s of the split-K
+  * decode (M=12) linears on the four Qwen3-VL-32B-like shapes: weight GB/s of the INT8 decode
     GEMV (x pre-quantized) and end to end (rotate+quantize + GEMV), replayed from HIP graphs
-    so that host launch gaps are not counted (eager times are reported beside them);
+    so that host launch gaps are not counted (eager times are reported beside them), and the
+    same for the W4A8 decode GEMV (INT4 group-scaled weights in the W4A8 block layout);
   * the W4A4 linear at M=4096, K=5376, N=10752 and the mixed profile with 20% W8A8 layers;
   * the 64-layer Qwen3-32B-shaped stack at M=2048 (all weights resident, 31 GB of INT8);
   * the CPU oracle on a bounded sample of the prefill workload (cpu_baseline).

@@ -87,8 +87,9 @@ int convrot_quantize_act(const void *x, int x_dtype, int64_t M, int64_t K, int g
  * Workspace bytes needed by convrot_linear (bits 8) / convrot_linear_w4a4 (bits 4) for this
  * shape; 0 on invalid arguments.  The workspace must be 256-byte aligned.  It is scratch: the
  * library initialises what it needs on the stream, so any contents are fine on entry and it holds
- * nothing useful afterwards.  convrot_gemm_i8_i32 with M <= 16 needs the same bits-8 size and
- * convrot_gemm_i4_i32 the bits-4 size.  The bits-4 workspace holds both operands' codes widened
+ * nothing useful afterwards.  The bits-8 workspace holds the quantized activations, so
+ * convrot_linear needs it only when it quantizes x itself; convrot_gemm_i8_i32 needs none (it
+ * accepts and ignores one); convrot_gemm_i4_i32 needs the bits-4 size.  The bits-4 workspace holds both operands' codes widened
  * to one byte each ((M + N) * K bytes) besides the activation codes and scales.
  */
 size_t convrot_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits);
@@ -99,7 +100,8 @@ size_t convrot_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits);
  *   x        bf16/fp32 [M, K] (x_dtype): rotated and quantized into the workspace first; or
  *   x = NULL: use the caller's xq int8 [M, K] and x_scale fp32 [M] from convrot_quantize_act.
  *   wq, w_scale from convrot_prepare_weight(bits = 8); bias fp32 [N] or NULL; y bf16 [M, N].
- * M <= 16 runs the weight-streaming split-K GEMV, larger M the MFMA GEMM.
+ * M <= 16 runs the weight-streaming GEMV, larger M the MFMA GEMM.  With x = NULL the workspace
+ * may be NULL.
  */
 int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_scale, int64_t M, int64_t N,
                    int64_t K, int group, const int8_t *wq, const float *w_scale, const float *bias, void *y,
@@ -162,7 +164,7 @@ size_t convrot_workspace_bytes_w4a8(int64_t M, int64_t N, int64_t K);
 
 /*
  * Integer core without scales, for exactness checks: acc int32 [M, N] = xq . wq^T (same kernels
- * and M-based dispatch as convrot_linear; the M <= 16 path needs the workspace).
+ * and M-based dispatch as convrot_linear; workspace unused, may be NULL).
  */
 int convrot_gemm_i8_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K, int32_t *acc,
                         void *workspace, size_t workspace_bytes, hipStream_t stream);

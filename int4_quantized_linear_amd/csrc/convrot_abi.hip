@@ -75,11 +75,10 @@ int hip_status(hipError_t e, const char *what)
 }
 
 // Workspace layout, each region 256-byte aligned; all of it is scratch (no initial contents):
-//   bits 8: [split-K counters + partial sums if M <= 16][xq int8 M*K][x_scale fp32 M]
+//   bits 8: [xq int8 M*K][x_scale fp32 M]
 //   bits 4: [xq packed M*K/2][x_scale fp16 (K/256)*M][unpacked codes (M+N)*K]
 struct WsLayout {
-    size_t gemv = 0, xq = 0, xs = 0, unp = 0, total = 0;
-    size_t gemv_bytes = 0;
+    size_t xq = 0, xs = 0, unp = 0, total = 0;
 };
 
 WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int bits)
@@ -87,11 +86,6 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int bits)
     WsLayout L;
     size_t off = 0;
     if (bits == 8) {
-        if (M <= 16) {
-            L.gemv = off;
-            L.gemv_bytes = convrot::gemv_i8_workspace_bytes(M, N, (int)K);
-            off += round256(L.gemv_bytes);
-        }
         L.xq = off;
         off += round256((size_t)(M * K));
         L.xs = off;
@@ -207,8 +201,7 @@ int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_
         !aligned(w_scale, 4) || !aligned(y, 16) || (bias && !aligned(bias, 4)))
         return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
     const WsLayout L = ws_layout(M, N, K, 8);
-    const bool need_ws = x != nullptr || (M <= 16 && L.gemv_bytes > 0);
-    if (need_ws && (!workspace || workspace_bytes < L.total || !aligned(workspace, 256)))
+    if (x && (!workspace || workspace_bytes < L.total || !aligned(workspace, 256)))
         return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes (got %zu)", who, L.total,
                     workspace ? workspace_bytes : (size_t)0);
     if (M == 0 || N == 0) return CONVROT_OK;
@@ -226,7 +219,7 @@ int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_
         x_scale = sx;
     }
     hipError_t e = M <= 16 ? convrot::launch_gemv_i8(xq, wq, x_scale, w_scale, bias, y, convrot::Epi::Bf16, M, N,
-                                                      (int)K, ws + L.gemv, stream)
+                                                      (int)K, stream)
                            : convrot::launch_gemm_i8(xq, wq, x_scale, w_scale, bias, y, convrot::Epi::Bf16, M, N,
                                                       (int)K, stream);
     return hip_status(e, M <= 16 ? "gemv_i8" : "gemm_i8");
@@ -241,14 +234,12 @@ int convrot_gemm_i8_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N
     if (M == 0 || N == 0) return CONVROT_OK;
     if (!xq || !wq || !acc) return fail(CONVROT_ERR_NULL, "%s: xq, wq and acc must be non-NULL", who);
     if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(acc, 16)) return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
-    const size_t need = M <= 16 ? round256(convrot::gemv_i8_workspace_bytes(M, N, (int)K)) : 0;
-    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
-        return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes", who, need);
-    if (M == 0 || N == 0) return CONVROT_OK;
+    (void)workspace;
+    (void)workspace_bytes;
     if ((rc = check_device())) return rc;
     if (M <= 16) {
         return hip_status(convrot::launch_gemv_i8(xq, wq, nullptr, nullptr, nullptr, acc, convrot::Epi::Int32, M, N,
-                                                  (int)K, workspace, stream),
+                                                  (int)K, stream),
                           "gemv_i8");
     }
     return hip_status(

@@ -5,49 +5,36 @@
 // ("Qwen3-VL-32B-...-INT8-ConvRot部署优化", section 运行时验证指标, output (1, 12, 5120)), so every
 // ConvRot linear there streams its whole INT8 weight once for 12 rows of work.
 //
-// Design: a workgroup (4 wavefronts) owns 64 weight rows and a slice of K, streamed in chunks
-// of 256 bytes per row through NST LDS stages.  Loads go global -> LDS directly
-// (buffer_load ... lds, 16 bytes per lane): one instruction moves 4 rows x 256 contiguous bytes,
-// so HBM sees whole 128-byte lines and long runs per row.  The <= 16 token rows of the chunk
-// (L2-resident) are staged the same way; tokens >= M and bytes past the slice read zeros through
-// out-of-bounds buffer offsets.  In LDS, 16-byte chunk c of row r sits at position c ^ (r & 15),
-// so the MFMA fragment reads (16 rows, same chunk) hit 16 distinct bank groups.  Wave w multiplies
-// K-step w of every chunk for all 64 rows with v_mfma_i32_16x16x64_i8 (rows = weight rows,
-// columns = tokens); the 4 waves' sums are added through LDS at the end.
-//
-// Split-K across workgroups (when the row tiles alone would not fill the chip): every split
-// stores its int32 partial sums into its own workspace slot with device-coherent stores, waits
-// for them to complete, then publishes a 64-bit arrival flag of its own (the call's generation
-// tag and its complement) and, once that store has completed, reads the flags of all splits of
-// its tile.  A split that sees every flag carrying the tag adds the other splits' partials to its
-// own (exact integer sums), runs the epilogue and clears the flags.  Store-then-read on both
-// sides guarantees that the last split to publish sees all flags; if several see them, they
-// write identical results.  There is no shared counter, so splits never contend on one address,
-// and stale workspace contents (other calls, other shapes, uninitialised memory) cannot match the
-// tag: the workspace needs no zero-fill.  Clearing the flags keeps a replay of the same launch
-// (same tag, e.g. from a captured graph) correct.  No cache-wide write-back/invalidate is needed:
-// partials and flags bypass the non-coherent per-XCD caches.
-#include <stdlib.h>
-
-#include <atomic>
-#include <chrono>
-
+// Design: a workgroup owns RB 16-row blocks of weights (16, 32 or 64 rows) and all of K; its NW
+// wavefronts split K into contiguous runs of 256-byte chunks.  Each wavefront streams its run on
+// its own, with no barrier in the main loop: per chunk it copies its rows' 256 bytes and the
+// <= 16 token rows' 256 bytes global -> LDS (buffer_load ... lds, 16 bytes per lane; one
+// instruction moves 4 rows x 256 contiguous bytes, i.e. whole 128-byte lines) into a private
+// ring of D stages, and waits for them with its own vmcnt.  In a stage, 16-byte chunk c of row
+// r sits at position c ^ (r & 15), so the MFMA fragment reads (16 rows, same chunk) hit 16
+// distinct bank groups.  Rows >= N, tokens >= M and bytes past K read zeros through
+// out-of-bounds buffer offsets.  v_mfma_i32_16x16x64_i8 (rows = weight rows, columns = tokens)
+// accumulates the whole run in int32 (|acc| <= 127^2 K < 2^31 for K <= 131072); the NW sums
+// are added once at the end through LDS (exact in any order) and the epilogue writes bf16 (or
+// the int32 sums).  There is no cross-workgroup split of K: joining partial sums across CUs
+// needs several trips to the device-coherent level, about a microsecond each, which is more
+// than a small decode call costs in total; small N gets more wavefronts per workgroup instead.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
 namespace convrot {
 namespace {
 
-constexpr int ROWS = 64;                 // weight rows per workgroup
 constexpr int KC = 256;                  // K bytes per row per chunk (4 MFMA K-steps)
-constexpr int NST = 4;                   // LDS stages (NST - 1 chunks in flight)
-constexpr int WBYTES = ROWS * KC;        // 16 KiB of weights per stage
-constexpr int XBYTES = 16 * KC;          // 4 KiB of tokens per stage
-constexpr int STG = WBYTES + XBYTES;
-constexpr int TARGET_WGS = 128;          // split-K only when fewer tiles than this (measured best)
-constexpr int MAX_SPLITS = 64;           // one flag per lane of a wavefront
+constexpr int D = 2;                     // LDS stages per wavefront
+constexpr int MAX_NW = 8;
+constexpr int TARGET_WAVES = 400;        // about 1.5 wavefronts per CU in all
+constexpr int MIN_CHUNKS = 5;            // per wavefront, to amortise its ramp-up and drain
+constexpr int LDS_BUDGET = 160 * 1024;
 constexpr uint32_t OOB = 0x80000000u;    // buffer offset past num_records -> loads return 0
 constexpr int NUM_RECORDS = 0x7ffffff0;
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct GemvParams {
     const int8_t *xq;
@@ -56,243 +43,202 @@ struct GemvParams {
     const float *sw;
     const float *bias;
     void *y;
-    int32_t *part;                 // [splits, M, N] partial sums
-    unsigned long long *flag;      // [tiles, splits] generation-tagged arrival flags
     int64_t N;
-    int M, K, splits;
-    unsigned gen;
+    int M, K;
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n only.
+// s_waitcnt immediate waiting for vmcnt <= n only (gfx9 encoding)
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
 
-template <Epi E>
-__device__ __forceinline__ void gemv_store(const GemvParams &p, int m, int64_t n, int32_t acc, float coef, float bias)
+template <int RB>
+constexpr int stage_bytes() { return (16 * RB + 16) * KC; }   // weight rows + 16 token rows
+
+// Copies of one chunk into a stage: copy j moves rows 4j + lane/16 of the stage (weight rows,
+// then the 16 token rows); lane%16 is the 16-byte position, holding chunk (lane%16) ^ (row & 15).
+// Offsets come precomputed per copy (row start + swizzled position, bit 31 set for rows past N or
+// tokens past M); here they get the chunk's K position, and bit 31 for pieces past K or for a
+// chunk past the run (out of range: zeros, no memory access).  Plain arithmetic rather than
+// selects, which the compiler would turn into branches around the loads.
+template <int RB>
+__device__ __forceinline__ void copy_chunk(uint8_t *st, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rx,
+                                           const uint32_t *wrow, const uint32_t *xrow, int k0, uint32_t dead, int K,
+                                           int cr, int px)
 {
-    if constexpr (E == Epi::Int32) {
-        static_cast<int32_t *>(p.y)[(int64_t)m * p.N + n] = acc;
-    } else {
-        const float v = __builtin_fmaf((float)acc, coef, bias);
-        static_cast<uint16_t *>(p.y)[(int64_t)m * p.N + n] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
+#pragma unroll
+    for (int j = 0; j < 4 * RB; ++j) {
+        const int rr = 4 * j + cr;
+        const uint32_t past = (uint32_t)(k0 + 16 * (px ^ (rr & 15)) >= K) << 31;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(st + 1024 * j), 16,
+                                                 (wrow[j] + (uint32_t)k0) | dead | past, 0, 0, 2);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int t = 4 * j + cr;
+        const uint32_t past = (uint32_t)(k0 + 16 * (px ^ t) >= K) << 31;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(st + 16 * RB * KC + 1024 * j), 16,
+                                                 (xrow[j] + (uint32_t)k0) | dead | past, 0, 0, 0);
     }
 }
 
-template <Epi E>
-__global__ void __launch_bounds__(256, 2) gemv_i8_kernel(GemvParams p)
+template <Epi E, int RB>
+__global__ void __launch_bounds__(64 * MAX_NW) gemv_i8_kernel(GemvParams p)
 {
-    // NST * STG = 80 KiB, so two workgroups share a CU's 160 KiB of LDS; the split-K arrival
-    // flag lives in the stage memory past the reduction area once the stages are done.
-    __shared__ __attribute__((aligned(16))) uint8_t smem[NST * STG];
-    int &last_flag = *reinterpret_cast<int *>(smem + 4 * 16 * 64 * 4);
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int WL = 4 * RB;                           // weight copies per chunk (4 rows each)
+    constexpr int LPC = WL + 4;                          // + 4 token copies
+    constexpr int STAGE = stage_bytes<RB>();
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int tile = blockIdx.x, split = blockIdx.y;
-    const int64_t n0 = (int64_t)tile * ROWS;
+    const int nw = blockDim.x >> 6;
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * RB);
     const int K = p.K;
-    const int steps = K / 64;
-    const int k_beg = (int)((int64_t)steps * split / p.splits) * 64;
-    const int k_end = (int)((int64_t)steps * (split + 1) / p.splits) * 64;
-    const int nchunks = (k_end - k_beg + KC - 1) / KC;
+    const int C = (K + KC - 1) / KC;
+    const int c_beg = C * w / nw;                        // nw <= C: every run has a chunk
+    const int c_end = C * (w + 1) / nw;
+    const int n = c_end - c_beg;
+    const int r = lane & 15, q = lane >> 4;
+    const int M = p.M;
+    const int m = r;
 
-    // Load geometry.  Weights: instruction i (0..3) of wave w fills rows 16w+4i .. +3 of a stage,
-    // lane -> row +lane/16 at 16-byte position lane%16, which holds chunk (lane%16) ^ (row & 15).
-    // Tokens: wave w fills token rows 4w .. 4w+3 the same way.
-    const int p16 = lane & 15, q4 = lane >> 4;
-    const __amdgpu_buffer_rsrc_t rw =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(p.wq + n0 * K), (short)0, NUM_RECORDS, 0x00020000);
+    // epilogue operands first, so that their latency hides under the main loop
+    float coef[RB][4], bia[RB][4];
+    if (E == Epi::Bf16 && w == 0) {
+        const float sxm = p.sx[m < M ? m : 0];
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t nn = n0 + 16 * b + 4 * q + v;
+                const int64_t nc = nn < p.N ? nn : 0;
+                coef[b][v] = sxm * p.sw[nc];
+                bia[b][v] = p.bias ? p.bias[nc] : 0.0f;
+            }
+    }
+
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t *>(p.wq + n0 * K), (short)0, NUM_RECORDS, 0x00020000);
     const __amdgpu_buffer_rsrc_t rx =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(p.xq), (short)0, NUM_RECORDS, 0x00020000);
-    uint32_t offw[4], kw[4];
+    uint8_t *ring = smem + w * (D * STAGE);
+    const int cr = lane >> 4, px = lane & 15;
+    uint32_t wrow[WL], xrow[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * i + q4;
-        kw[i] = (uint32_t)(k_beg + 16 * (p16 ^ (r & 15)));
-        offw[i] = n0 + r < p.N ? (uint32_t)(r * K) + kw[i] : OOB;
+    for (int j = 0; j < WL; ++j) {
+        const int rr = 4 * j + cr;
+        wrow[j] = ((uint32_t)(rr * K + 16 * (px ^ (rr & 15)))) | ((uint32_t)(n0 + rr >= p.N) << 31);
     }
-    const int t = 4 * w + q4;
-    const uint32_t kx = (uint32_t)(k_beg + 16 * (p16 ^ (t & 15)));
-    const uint32_t offx = t < p.M ? (uint32_t)(t * K) + kx : OOB;
-
-    auto issue = [&](int g) {
-        uint8_t *st = smem + (g % NST) * STG;
-        const uint32_t kk = (uint32_t)(g * KC);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t o = (offw[i] != OOB && kw[i] + kk < (uint32_t)k_end) ? offw[i] + kk : OOB;
-            // weights are read once: nontemporal (aux bit 1)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(st + (16 * w + 4 * i) * KC), 16, o, 0, 0, 2);
-        }
-        const uint32_t o = (offx != OOB && kx + kk < (uint32_t)k_end) ? offx + kk : OOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(st + WBYTES + 4 * w * KC), 16, o, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+        const int t = 4 * j + cr;
+        xrow[j] = ((uint32_t)(t * K + 16 * (px ^ t))) | ((uint32_t)(t >= M) << 31);
+    }
+    // chunk c of this wavefront = K bytes [256 (c_beg + c), +256)
+    auto load = [&](int slot, int c) {
+        copy_chunk<RB>(ring + slot * STAGE, rw, rx, wrow, xrow, (c_beg + c) * KC, (uint32_t)(c >= n) << 31, K, cr, px);
     };
 
-    // Fragment addressing: wave w reads K-step w of a chunk; lane -> row/token lane%16, 16-byte
-    // chunk 4w + lane/16 at position (4w + lane/16) ^ (lane%16).
-    const int fpos = 16 * ((4 * w + q4) ^ p16);
-    const int arow = p16 * KC + fpos;
-    v4i acc[4] = {v4i{}, v4i{}, v4i{}, v4i{}};
-
-    if (nchunks > 0) issue(0);
-    if (nchunks > 1) issue(1);
-    if (nchunks > 2) issue(2);
-
-    // Outputs of this thread after the cross-wave reduction: entry idx = threadIdx + 256u of the
-    // [16 values][64 lanes] accumulator image; the epilogue's scales and bias are fetched now,
-    // behind the first chunks' loads, so that their latency hides under the main loop.
-    int mm[4];
-    int64_t nn[4];
-    bool ok[4];
-    float coef[4], bia[4];
+    v4i acc[RB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int idx = threadIdx.x + 256 * u;
-        const int v = idx >> 6, l = idx & 63;
-        mm[u] = l & 15;
-        nn[u] = n0 + 16 * (v >> 2) + 4 * (l >> 4) + (v & 3);
-        ok[u] = mm[u] < p.M && nn[u] < p.N;
-        coef[u] = 0.0f;
-        bia[u] = 0.0f;
-        if constexpr (E == Epi::Bf16) {
-            // branch-free (clamped indices), so the loads are all in flight together
-            const int mc = mm[u] < p.M ? mm[u] : p.M - 1;
-            const int64_t nc = nn[u] < p.N ? nn[u] : p.N - 1;
-            coef[u] = p.sx[mc] * p.sw[nc];
-            bia[u] = p.bias ? p.bias[nc] : 0.0f;
+    for (int b = 0; b < RB; ++b) acc[b] = v4i{};
+
+    auto compute = [&](int slot) {
+        // this chunk has landed once at most the next chunk's copies remain in flight
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm((D - 1) * LPC));
+        const uint8_t *st = ring + slot * STAGE;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int pos = 16 * ((4 * kk + q) ^ r);
+            const v4i xb = *reinterpret_cast<const v4i *>(st + 16 * RB * KC + r * KC + pos);
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+                const v4i a = *reinterpret_cast<const v4i *>(st + (16 * b + r) * KC + pos);
+                acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xb, acc[b], 0, 0, 0);
+            }
+        }
+    };
+
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        load(j, j);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // whole rounds of D chunks, so that the loop body has no branch (a join would make the
+    // compiler drain every load in flight); chunks past the run are zeros and add nothing
+    for (int c0 = 0; c0 < n; c0 += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            compute(j);
+            // the fragment reads of this stage must finish before its refill lands
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            load(j, c0 + j + D);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    for (int g = 0; g < nchunks; ++g) {
-        // chunk g has landed once at most the loads of chunks g+1, g+2 (5 per wave each) remain
-        if (g + 2 < nchunks) __builtin_amdgcn_s_waitcnt(waitcnt_vm(10));
-        else if (g + 1 < nchunks) __builtin_amdgcn_s_waitcnt(waitcnt_vm(5));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        // Barrier without a memory fence: a fence would make the compiler wait for every load in
-        // flight (vmcnt 0) and serialise the pipeline.  The explicit vmcnt wait above covers this
-        // wave's chunk-g loads, lgkmcnt(0) retires its LDS reads of the stage about to be refilled.
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (g + 3 < nchunks) issue(g + 3);
-        const uint8_t *st = smem + (g % NST) * STG;
-        const v4i xb = *reinterpret_cast<const v4i *>(st + WBYTES + arow);
+    if (nw > 1) {
+        __syncthreads();                                 // every ring is idle: reuse the LDS
+        int32_t *red = reinterpret_cast<int32_t *>(smem);   // [nw][RB * 4][64]
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const v4i wa = *reinterpret_cast<const v4i *>(st + 16 * b * KC + arow);
-            acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa, xb, acc[b], 0, 0, 0);
+        for (int b = 0; b < RB; ++b)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) red[(w * RB * 4 + 4 * b + v) * 64 + lane] = acc[b][v];
+        __syncthreads();
+        if (w != 0) return;
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                int32_t s = red[(4 * b + v) * 64 + lane];
+                for (int ww = 1; ww < nw; ++ww) s += red[(ww * RB * 4 + 4 * b + v) * 64 + lane];
+                acc[b][v] = s;
+            }
+    }
+    if (m >= M) return;
+    // 16x16 layout: lane holds token m = lane%16 and rows 4*(lane/16) + v of each 16-row block
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t nn = n0 + 16 * b + 4 * q + v;
+            if (nn >= p.N) continue;
+            if constexpr (E == Epi::Int32) {
+                static_cast<int32_t *>(p.y)[(int64_t)m * p.N + nn] = acc[b][v];
+            } else {
+                const float yv = __builtin_fmaf((float)acc[b][v], coef[b][v], bia[b][v]);
+                static_cast<uint16_t *>(p.y)[(int64_t)m * p.N + nn] = (uint16_t)(pack_bf16x2(yv, 0.0f) & 0xffffu);
+            }
         }
-    }
-
-    // 16x16 accumulator layout: lane holds token m = lane%16 and weight rows 4*(lane/16) + v.
-    __syncthreads();                         // all waves are done with the stages
-    int32_t *red = reinterpret_cast<int32_t *>(smem);   // [4 waves][16 values][64 lanes]
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) red[(w * 16 + 4 * b + v) * 64 + lane] = acc[b][v];
-    __syncthreads();
-
-    int32_t sum[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int idx = threadIdx.x + 256 * u;
-        sum[u] = red[idx] + red[1024 + idx] + red[2048 + idx] + red[3072 + idx];
-    }
-
-    if (p.splits == 1) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (ok[u]) gemv_store<E>(p, mm[u], nn[u], sum[u], coef[u], bia[u]);
-        return;
-    }
-
-    const int64_t MN = (int64_t)p.M * p.N;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-        if (ok[u])
-            __hip_atomic_store(&p.part[split * MN + (int64_t)mm[u] * p.N + nn[u]], sum[u], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);     // this thread's partial stores have completed
-    __syncthreads();
-    if (w == 0) {
-        const unsigned long long tag = ((unsigned long long)p.gen << 32) | (unsigned)~p.gen;
-        unsigned long long *fl = p.flag + (int64_t)tile * p.splits;
-        if (lane == 0) __hip_atomic_store(fl + split, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0); // the flag store has completed before any flag is read
-        const bool seen = lane >= p.splits || lane == split ||
-                          __hip_atomic_load(fl + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
-        const bool all = __builtin_amdgcn_ballot_w64(!seen) == 0;
-        // every split has arrived: clear the flags (all were written already) for a replay
-        if (all && lane < p.splits) __hip_atomic_store(fl + lane, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (lane == 0) last_flag = all;
-    }
-    __syncthreads();
-    if (!last_flag) return;
-    // Sum the other splits' partials (integer addition: exact in any order).  The loads of a
-    // batch of 8 splits x 4 outputs are independent, so they are in flight together instead of
-    // paying one memory round trip per split.
-    const int32_t *part[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) part[u] = p.part + (ok[u] ? (int64_t)mm[u] * p.N + nn[u] : 0);
-    for (int s0 = 0; s0 < p.splits; s0 += 8) {
-        int32_t v[4][8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int s = s0 + j;
-            const bool use = s < p.splits && s != split;
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                v[u][j] = (use && ok[u]) ? __hip_atomic_load(part[u] + s * MN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                         : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sum[u] += v[u][j];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-        if (ok[u]) gemv_store<E>(p, mm[u], nn[u], sum[u], coef[u], bia[u]);
 }
 
-int forced_splits()
-{
-    static const int v = [] {
-        const char *e = getenv("CONVROT_GEMV_SPLITS");
-        return e ? atoi(e) : 0;
-    }();
-    return v;
-}
+struct Plan {
+    int rb, nw;
+    int64_t tiles;
+};
 
-unsigned next_generation()
+// Rows per workgroup: 64 from N = 16384 on, 32 from N = 4096, else 16 (more workgroups for small
+// N; each one re-reads the tokens).  Wavefronts per workgroup: about TARGET_WAVES in all, each
+// with at least MIN_CHUNKS chunks, within the LDS budget (D stages per wavefront).  Both
+// measured on the decode shapes (N x K = 8192/1024/25600 x 5120, 5120 x 25600): fewer,
+// longer-running wavefronts beat many short ones.
+Plan plan(int64_t N, int K)
 {
-    // Seeded per process so that leftovers from another process never carry the current tag.
-    static std::atomic<unsigned> gen{(unsigned)std::chrono::steady_clock::now().time_since_epoch().count() | 1u};
-    unsigned g = gen.fetch_add(1) + 1;
-    return g ? g : gen.fetch_add(1) + 1;
+    Plan pl;
+    pl.rb = N >= 16384 ? 4 : N >= 4096 ? 2 : 1;
+    pl.tiles = (N + 16 * pl.rb - 1) / (16 * pl.rb);
+    const int C = (K + KC - 1) / KC;
+    int64_t nw = (TARGET_WAVES + pl.tiles - 1) / pl.tiles;
+    if (nw > C / MIN_CHUNKS) nw = C / MIN_CHUNKS;
+    const int per_wave = D * (pl.rb == 4 ? stage_bytes<4>() : pl.rb == 2 ? stage_bytes<2>() : stage_bytes<1>());
+    if (nw > LDS_BUDGET / per_wave) nw = LDS_BUDGET / per_wave;
+    if (nw > MAX_NW) nw = MAX_NW;
+    pl.nw = nw < 1 ? 1 : (int)nw;
+    return pl;
 }
 
 } // namespace
 
-int gemv_i8_splits(int64_t N, int K)
-{
-    const int64_t tiles = (N + ROWS - 1) / ROWS;
-    int s = forced_splits() > 0 ? forced_splits() : (int)((TARGET_WGS + tiles - 1) / tiles);
-    int smax = K / KC > 1 ? K / KC : 1;            // at least one full chunk per split
-    if (smax > MAX_SPLITS) smax = MAX_SPLITS;
-    if (s > smax) s = smax;
-    return s < 1 ? 1 : s;
-}
-
-size_t gemv_i8_workspace_bytes(int64_t M, int64_t N, int K)
-{
-    const int64_t tiles = (N + ROWS - 1) / ROWS;
-    const int s = gemv_i8_splits(N, K);
-    if (s == 1) return 0;
-    return (size_t)(tiles * s * 8 + (int64_t)s * M * N * 4);
-}
-
 hipError_t launch_gemv_i8(const int8_t *xq, const int8_t *wq, const float *sx, const float *sw, const float *bias,
-                          void *y, Epi epi, int64_t M, int64_t N, int K, void *ws, hipStream_t stream)
+                          void *y, Epi epi, int64_t M, int64_t N, int K, hipStream_t stream)
 {
     if (M <= 0 || N <= 0) return hipSuccess;
     GemvParams p;
@@ -305,16 +251,25 @@ hipError_t launch_gemv_i8(const int8_t *xq, const int8_t *wq, const float *sx, c
     p.N = N;
     p.M = (int)M;
     p.K = K;
-    p.splits = gemv_i8_splits(N, K);
-    const int64_t tiles = (N + ROWS - 1) / ROWS;
-    p.flag = static_cast<unsigned long long *>(ws);
-    p.part = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(ws) + tiles * p.splits * 8);
-    p.gen = next_generation();
-    const dim3 grid((unsigned)tiles, (unsigned)p.splits), block(256);
-    if (epi == Epi::Int32)
-        hipLaunchKernelGGL(gemv_i8_kernel<Epi::Int32>, grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL(gemv_i8_kernel<Epi::Bf16>, grid, block, 0, stream, p);
+    const Plan pl = plan(N, K);
+    const dim3 grid((unsigned)pl.tiles), block(64 * pl.nw);
+    const size_t lds =
+        (size_t)pl.nw * D * (pl.rb == 4 ? stage_bytes<4>() : pl.rb == 2 ? stage_bytes<2>() : stage_bytes<1>());
+    if (epi == Epi::Int32) {
+        if (pl.rb == 4)
+            hipLaunchKernelGGL((gemv_i8_kernel<Epi::Int32, 4>), grid, block, lds, stream, p);
+        else if (pl.rb == 2)
+            hipLaunchKernelGGL((gemv_i8_kernel<Epi::Int32, 2>), grid, block, lds, stream, p);
+        else
+            hipLaunchKernelGGL((gemv_i8_kernel<Epi::Int32, 1>), grid, block, lds, stream, p);
+    } else {
+        if (pl.rb == 4)
+            hipLaunchKernelGGL((gemv_i8_kernel<Epi::Bf16, 4>), grid, block, lds, stream, p);
+        else if (pl.rb == 2)
+            hipLaunchKernelGGL((gemv_i8_kernel<Epi::Bf16, 2>), grid, block, lds, stream, p);
+        else
+            hipLaunchKernelGGL((gemv_i8_kernel<Epi::Bf16, 1>), grid, block, lds, stream, p);
+    }
     return hipGetLastError();
 }
 

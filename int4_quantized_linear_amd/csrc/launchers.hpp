@@ -19,12 +19,10 @@ enum class Epi { Bf16 = 0, Int32 = 1 };
 hipError_t launch_gemm_i8(const int8_t *xq, const int8_t *wq, const float *sx, const float *sw, const float *bias,
                           void *y, Epi epi, int64_t M, int64_t N, int K, hipStream_t stream);
 
-// Same contraction for M <= 16 (weight streaming, split-K).  `ws` is scratch of
-// gemv_i8_workspace_bytes() bytes (0 when K is not split); its contents on entry do not matter.
-int gemv_i8_splits(int64_t N, int K);
-size_t gemv_i8_workspace_bytes(int64_t M, int64_t N, int K);
+// Same contraction for M <= 16 (weight streaming; K split among the wavefronts of a workgroup,
+// no scratch memory).
 hipError_t launch_gemv_i8(const int8_t *xq, const int8_t *wq, const float *sx, const float *sw, const float *bias,
-                          void *y, Epi epi, int64_t M, int64_t N, int K, void *ws, hipStream_t stream);
+                          void *y, Epi epi, int64_t M, int64_t N, int K, hipStream_t stream);
 
 // W4A4: y = bf16(sum_g acc_g * sx[m,g] * sw[n,g] + bias[n]) with packed int4 operands and
 // fp16 group scales (group = 256), or the unscaled int32 total sum_k cx*cw (scales ignored).

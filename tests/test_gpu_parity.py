@@ -98,7 +98,7 @@ def test_prepare_weight_same_as_quantize_act(cr):
 # ------------------------------------------------------------------ integer core (rule b)
 
 GEMM_CASES = [
-    # M, N, K  (M <= 16 runs the split-K GEMV kernel)
+    # M, N, K  (M <= 16 runs the decode GEMV kernel)
     (1, 64, 64), (12, 1000, 5120), (16, 264, 320), (12, 8192, 5120), (3, 5120, 25600),
     (17, 8, 64), (300, 264, 320), (513, 1000, 5376), (256, 256, 128), (1000, 1280, 1024),
 ]
@@ -226,7 +226,7 @@ def test_linear_empty_and_repeat(cr):
     wq, ws = cr.prepare_weight(w, 256, 8)
     y = cr.linear(torch.empty(0, 256, dtype=torch.bfloat16, device=DEV), wq, ws)
     assert y.shape == (0, 64)
-    # two decode calls in a row with different inputs reuse the split-K workspace correctly
+    # two decode calls in a row with different inputs
     for seed in (1, 2):
         x = workloads.heavy_tailed_acts(12, 256, cfg=98, layer=seed).to(DEV)
         y = cr.linear(x, wq, ws)
