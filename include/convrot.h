@@ -89,8 +89,9 @@ int convrot_quantize_act(const void *x, int x_dtype, int64_t M, int64_t K, int g
  * library initialises what it needs on the stream, so any contents are fine on entry and it holds
  * nothing useful afterwards.  The bits-8 workspace holds the quantized activations, so
  * convrot_linear needs it only when it quantizes x itself; convrot_gemm_i8_i32 needs none (it
- * accepts and ignores one); convrot_gemm_i4_i32 needs the bits-4 size.  The bits-4 workspace holds both operands' codes widened
- * to one byte each ((M + N) * K bytes) besides the activation codes and scales.
+ * accepts and ignores one); convrot_gemm_i4_i32 needs the bits-4 size.  Besides the activation
+ * codes and scales, the bits-4 workspace holds both operands re-encoded as FP6 in matrix-core
+ * order (1536 bytes per 32 rows x 64 channels, (ceil(M/32) + ceil(N/32)) * K/64 pieces).
  */
 size_t convrot_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits);
 

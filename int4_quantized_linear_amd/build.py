@@ -19,6 +19,9 @@ SOURCES = ["convrot_abi.hip", "rotate_quant.hip", "gemm_i8.hip", "gemv_i8.hip", 
 # Packed-fp32 VALU forms are disabled on purpose: plain fp32 code is emitted instead.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-Wno-unused-command-line-argument"]
+# Per-source extras.  The W4A4 GEMM keeps its group fold where it is written: machine sinking
+# would move it past the load-issue branches, after the barrier, and spill.
+SOURCE_FLAGS = {"gemm_w4a4.hip": ["-mllvm", "-disable-machine-sink"]}
 
 
 def _hipcc() -> str:
@@ -29,7 +32,7 @@ def _hipcc() -> str:
 
 
 def _compile(src: str, obj: str) -> None:
-    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -76,9 +76,9 @@ int hip_status(hipError_t e, const char *what)
 
 // Workspace layout, each region 256-byte aligned; all of it is scratch (no initial contents):
 //   bits 8: [xq int8 M*K][x_scale fp32 M]
-//   bits 4: [xq packed M*K/2][x_scale fp16 (K/256)*M][unpacked codes (M+N)*K]
+//   bits 4: [xq packed M*K/2][x_scale fp16 (K/256)*M][FP6 tiles of both operands]
 struct WsLayout {
-    size_t xq = 0, xs = 0, unp = 0, total = 0;
+    size_t xq = 0, xs = 0, tiles = 0, total = 0;
 };
 
 WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int bits)
@@ -95,8 +95,8 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int bits)
         off += round256((size_t)(M * K / 2));
         L.xs = off;
         off += round256((size_t)(M * (K / 256) * 2));
-        L.unp = off;
-        off += round256(convrot::w4a4_unpacked_bytes(M, N, (int)K));
+        L.tiles = off;
+        off += round256(convrot::w4a4_tiled_bytes(M, N, (int)K));
     }
     L.total = off;
     return L;
@@ -279,7 +279,7 @@ int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uin
         x_scale = reinterpret_cast<const uint16_t *>(ws + L.xs);
     }
     return hip_status(convrot::launch_gemm_w4a4(xq, wq, x_scale, w_scale, bias, y, convrot::Epi::Bf16, M, N, (int)K,
-                                                static_cast<uint8_t *>(workspace) + L.unp, stream),
+                                                static_cast<uint8_t *>(workspace) + L.tiles, stream),
                       "gemm_w4a4");
 }
 
@@ -367,7 +367,7 @@ int convrot_gemm_i4_i32(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t
         return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes", who, L.total);
     if ((rc = check_device())) return rc;
     return hip_status(convrot::launch_gemm_w4a4(xq, wq, nullptr, nullptr, nullptr, acc, convrot::Epi::Int32, M, N,
-                                                (int)K, static_cast<uint8_t *>(workspace) + L.unp, stream),
+                                                (int)K, static_cast<uint8_t *>(workspace) + L.tiles, stream),
                       "gemm_w4a4");
 }
 

@@ -1,52 +1,85 @@
-// gemm_w4a4.hip -- W4A4 ConvRot linear on the INT8 MFMA core (gfx950).
+// gemm_w4a4.hip -- W4A4 ConvRot linear on the FP6 matrix instructions of gfx950.
 //
 // Both operands were rotated by the grouped Hadamard and quantized to 4-bit codes with one fp16
 // scale per (row, 256-channel group) ("minimax-h3-nvfp4-convrot核心原理", section 五: W4A4 rotates
-// activations and weights and quantizes to 4 bits, RTN).  gfx950 has no INT4 matrix instruction,
-// so the codes are widened to INT8 and run through v_mfma_i32_32x32x32_i8:
+// activations and weights and quantizes to 4 bits, RTN):
 //   y[m,n] = sum_g ( sum_{k in g} cx[m,k] cw[n,k] ) * sx[g,m] * sw[g,n] + bias[n]
-// Each group's integer dot products are exact; they are scaled and summed in fp32 in
-// increasing group order.
+// gfx950 has no INT4 matrix instruction, but every 4-bit code (-8..7) is exactly an FP6 E3M2
+// value (OCP MX: sign, 3 exponent bits with bias 3, 2 mantissa bits), and
+// v_mfma_scale_f32_32x32x64_f8f6f4 multiplies FP6 operands at twice the INT8 rate with fp32
+// accumulation.  A group's 256 products are integers of magnitude <= 64 * 256, so its fp32 sum
+// is exact: the same integer the INT8 core would give.  The block-scale operands stay at 2^0;
+// the fp16 scales are applied afterwards in fp32, group by group in increasing order.
 //
 // Two kernels:
-//  * unpack: packed nibbles -> int8 bytes 16*c (exact; low nibble (d << 4) & 0xF0F0F0F0, high
-//    nibble d & 0xF0F0F0F0).  A packed dword's 8 codes come out as [c0 c2 c4 c6 | c1 c3 c5 c7]:
-//    a fixed permutation inside every 8 channels, identical for tokens and weights, so every
-//    dot product (and every 256-channel group) is unchanged.  The factor 16 * 16 = 256 is
-//    removed with the scales;
-//  * GEMM: the pipeline of the INT8 GEMM (persistent, XCD-aware tile order, 128-byte K-tiles
-//    loaded global -> LDS with buffer_load ... lds, swizzled conflict-free fragment reads), with
-//    3 LDS stages of 256 weight rows + 128 token rows.  8 wavefronts each own 64x64 outputs as
-//    2x2 blocks of 32x32, with an int32 accumulator for the current group and an fp32 one for
-//    the sum over groups (64 + 64 registers per lane).  A group is 2 K-tiles.  The group's
-//    integer block is folded into the fp32 accumulator block by block inside the next group's
-//    first MFMA sub-step, whose MFMAs start from a zero accumulator, so the fold's VALU work
-//    overlaps the matrix pipe; the tile's last group is folded before its epilogue.  The
-//    group's scales and the tile's bias are loaded into small LDS rings with the K-tiles.
+//  * tile: packed nibbles -> FP6 in the order the MFMA consumes them.  Per 32-row block and
+//    64-channel K-step one 1536-byte piece; lane l = (r = l % 32, h = l / 32) owns the 32 codes
+//    of row r at channels 64 ks + 32 h + s (s = 0..31), 6 bits each at bit 6 s of a 24-byte
+//    string whose first 16 bytes sit at 16 l and last 8 at 1024 + 8 l.  Pieces are ordered
+//    [row block][K-step], so a row block's two K-steps of a 128-channel K-tile are 3 KiB of
+//    contiguous memory that 16-byte loads-to-LDS copy verbatim, and a fragment is one 16-byte
+//    and one 8-byte LDS read, both conflict-free.  Rows past the operand's end are zeros;
+//  * GEMM: persistent, XCD-aware tile order, 256 weight rows x 128 token rows per workgroup,
+//    K-tiles of 128 channels (3 KiB per row block) loaded global -> LDS with buffer_load ... lds
+//    into NST stages.  8 wavefronts each own 64x64 outputs as 2x2 blocks of 32x32, with an fp32
+//    accumulator for the current 256-group and one for the sum over groups (64 + 64 registers
+//    per lane).  A group's block is folded into the sum right before the next group's first
+//    MFMA restarts it from zero; the scale product sx[m] * sw[n] of a block comes from one
+//    f16 MFMA (an outer product), so the fold costs one FMA per output.  The tile's last group
+//    is folded before its epilogue.  The group's scales and the tile's bias ride in small LDS
+//    rings with the K-tiles.
+//
+// Built with machine sinking off (-mllvm -disable-machine-sink): otherwise the fold's FMAs and
+// MFMAs are sunk past the load-issue branches into the next block, after the barrier, where
+// they no longer overlap the matrix pipe and the register pressure spills.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
 namespace convrot {
 namespace {
 
-constexpr int BN = 256, BM = 128, BK = 128, NST = 3;
-constexpr int WB = BN * BK, XB = BM * BK;         // bytes per stage: 32 KiB + 16 KiB
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+
+constexpr int PIECE = 1536;                       // one 32-row block x 64 channels of FP6
+constexpr int CHUNK = 2 * PIECE;                  // one 32-row block x one 128-channel K-tile
+constexpr int BN = 256, BM = 128, BK = 128, NST = 4;
+constexpr int WB = (BN / 32) * CHUNK, XB = (BM / 32) * CHUNK;   // 24 KiB + 12 KiB per stage
 constexpr int STAGE = WB + XB;
-constexpr int SC_OFF = NST * STAGE;               // 144 KiB
+constexpr int DUMMY_OFF = NST * STAGE;            // 1 KiB target of the padding loads
+constexpr int SC_OFF = DUMMY_OFF + 1024;
 // One group's scales: sw as packed fp16 (512 B), then sx with one fp16 per dword (512 B).
 constexpr int SC_BYTES = 2 * BN + 4 * BM;
 constexpr int NSC = 4;                            // group-scale ring
 constexpr int BIAS_OFF = SC_OFF + NSC * SC_BYTES;
 constexpr int NBIAS = 4;                          // per-tile bias ring (fp32)
-constexpr int SMEM = BIAS_OFF + NBIAS * BN * 4;
+constexpr int ZERO_OFF = BIAS_OFF + NBIAS * BN * 4; // 16 zero bytes
+constexpr int SMEM = ZERO_OFF + 16;
+static_assert(SMEM <= 160 * 1024, "LDS budget");
 constexpr int NTHREADS = 512;
 constexpr int GROUP_M = 8;
 constexpr uint32_t OOB = 0x80000000u;
 constexpr int NUM_RECORDS = 0x7ffffff0;
 
+// E3M2 bit patterns of the 4-bit codes: nibble v is the code v (v < 8) or v - 16 (v >= 8).
+constexpr uint32_t e3m2_of_magnitude(int a)   // a = 0..8
+{
+    return a == 0 ? 0u : a == 1 ? 12u : a == 2 ? 16u : a == 3 ? 18u : a == 4 ? 20u : a == 5 ? 21u : a == 6 ? 22u
+                                                                                        : a == 7 ? 23u : 24u;
+}
+constexpr uint64_t e3m2_table(bool negative)   // 8 entries of 6 bits: nibbles 0..7 or 8..15
+{
+    uint64_t t = 0;
+    for (int i = 0; i < 8; ++i)
+        t |= (uint64_t)(negative ? 0x20u | e3m2_of_magnitude(8 - i) : e3m2_of_magnitude(i)) << (6 * i);
+    return t;
+}
+constexpr uint64_t E3M2_POS = e3m2_table(false), E3M2_NEG = e3m2_table(true);
+
 struct W4Params {
-    const int8_t *xq;     // unpacked codes x16 [M, K]
-    const int8_t *wq;     // unpacked codes x16 [N, K]
+    const uint8_t *xt;    // tokens, FP6 tiles [ceil(M/32)][K/64][1536]
+    const uint8_t *wt;    // weights, FP6 tiles [ceil(N/32)][K/64][1536]
     const uint16_t *sx;   // [G, M] fp16
     const uint16_t *sw;   // [G, N] fp16
     const float *bias;
@@ -57,8 +90,6 @@ struct W4Params {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
 
@@ -77,25 +108,42 @@ __device__ __forceinline__ void tile_of(int pid, int T, int tiles_m, int tiles_n
     tn = r / gsz;
 }
 
-// ---------------------------------------------------------------------------------------------
-// unpack: 16 packed bytes (32 codes) per thread per step -> 32 int8 bytes
-
-__global__ void __launch_bounds__(256) unpack_i4_kernel(const uint8_t *src, int8_t *dst, int64_t n16)
+__device__ __forceinline__ v16f mfma_fp6(const v8i &a, const v8i &b, const v16f &c)
 {
+    // cbsz = blgp = 3: both operands FP6 E3M2; scale operands 127 = 2^0
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 3, 3, 0, 127, 0, 127);
+}
+
+// ---------------------------------------------------------------------------------------------
+// tile: one thread per (piece, lane): 16 packed bytes (32 codes) in, 24 bytes out.
+
+__global__ void __launch_bounds__(256) tile_fp6_kernel(const uint8_t *src, uint8_t *dst, int64_t R, int K,
+                                                       uint32_t pieces)
+{
+    const uint32_t KS = (uint32_t)K >> 6;
+    const int64_t n = (int64_t)pieces * 64;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
-        const v4u d = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(src) + i);
-        v4u lo, hi;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const uint32_t pc = (uint32_t)(i >> 6), l = (uint32_t)i & 63;
+        const uint32_t rb = pc / KS, ks = pc - rb * KS;
+        const int64_t row = 32 * (int64_t)rb + (l & 31);
+        v4u d = {0u, 0u, 0u, 0u};
+        if (row < R)
+            d = __builtin_nontemporal_load(
+                reinterpret_cast<const v4u *>(src + row * (K >> 1) + 32 * (int64_t)ks + 16 * (l >> 5)));
+        uint32_t o[6] = {0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            // packed dword e -> [lows | highs] = output dwords 2e, 2e+1
-            const uint32_t l = (d[e] << 4) & 0xF0F0F0F0u, h = d[e] & 0xF0F0F0F0u;
-            if (e < 2) { lo[2 * e] = l; lo[2 * e + 1] = h; }
-            else { hi[2 * e - 4] = l; hi[2 * e - 3] = h; }
+        for (int s = 0; s < 32; ++s) {
+            // code s = channel 64 ks + 32 h + s: byte s/2, low nibble for even s
+            const uint32_t v = (d[s >> 3] >> (4 * (s & 7))) & 15u;
+            const uint32_t c = (uint32_t)(((v & 8u) ? E3M2_NEG : E3M2_POS) >> (6 * (v & 7u))) & 63u;
+            const int bit = 6 * s, dw = bit >> 5, off = bit & 31;
+            o[dw] |= c << off;
+            if (off > 26) o[dw + 1] |= c >> (32 - off);
         }
-        v4u *o = reinterpret_cast<v4u *>(dst) + 2 * i;
-        o[0] = lo;
-        o[1] = hi;
+        uint8_t *piece = dst + (int64_t)pc * PIECE;
+        *reinterpret_cast<v4u *>(piece + 16 * l) = v4u{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<v2u *>(piece + 1024 + 8 * l) = v2u{o[4], o[5]};
     }
 }
 
@@ -111,34 +159,42 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
     const int K = p.K;
     const int KT = K / BK;                     // even: K % 256 == 0
     const int G = K / 256;
+    const int KSTRIDE = (K / 64) * PIECE;      // bytes between consecutive row blocks
     const int T = p.tiles_m * p.tiles_n;
     const int ntiles = (T - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
     const int total = ntiles * KT;
+    const int nblk_w = (int)((p.N + 31) >> 5), nblk_x = (int)((p.M + 31) >> 5);
 
-    // Load geometry: weights, instruction i (0..3) of wave w fills rows 8*(8i+w) .. +7; tokens,
-    // instruction i (0..1) fills rows 8*(8i+w) .. +7; lane -> row +lane/8, 16-byte position
-    // lane%8 holding K chunk (lane%8) ^ swz(row).
-    int lrow[4], lchunk[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        lrow[i] = 8 * (8 * i + w) + (lane >> 3);
-        lchunk[i] = (lane & 7) ^ swz(lrow[i]);
-    }
-
+    // Load geometry: a K-tile is 24 weight and 12 token 1 KiB pieces; wave w issues weight
+    // pieces w, w + 8, w + 16 and token pieces w and w + 8 (waves 4..7: a padding load to the
+    // 1 KiB dummy area instead, so every wave issues the same number of loads).  Piece d of a
+    // row-block chunk array is row block d / 3, third d % 3, and lands at LDS offset 1024 d.
     int ld_t = -1, ld_tm = 0, ld_tn = 0;
     __amdgpu_buffer_rsrc_t rw, rx;
-    uint32_t offw[4], offx[2];
+    // Per load: the lane's 16-byte position as voffset (with bit 31 set when the row block lies
+    // past the operand, so the load returns zeros without touching memory) and the wave-uniform
+    // rest (row block and third) in soffset.
+    const uint32_t lane16 = 16u * (uint32_t)lane;
+    uint32_t sow[3], sox[2], oobw[3], oobx[2];
     auto set_load_tile = [&](int t) {
         ld_t = t;
         tile_of((int)blockIdx.x + t * (int)gridDim.x, T, p.tiles_m, p.tiles_n, ld_tm, ld_tn);
-        const int64_t m0 = (int64_t)ld_tm * BM, n0 = (int64_t)ld_tn * BN;
-        rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(p.wq + n0 * K), (short)0, NUM_RECORDS, 0x00020000);
-        rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(p.xq + m0 * K), (short)0, NUM_RECORDS, 0x00020000);
+        const int bw0 = ld_tn * (BN / 32), bx0 = ld_tm * (BM / 32);
+        rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(p.wt + (int64_t)bw0 * KSTRIDE), (short)0,
+                                               NUM_RECORDS, 0x00020000);
+        rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(p.xt + (int64_t)bx0 * KSTRIDE), (short)0,
+                                               NUM_RECORDS, 0x00020000);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t o = (uint32_t)(lrow[i] * K + 16 * lchunk[i]);
-            offw[i] = n0 + lrow[i] < p.N ? o : OOB;
-            if (i < 2) offx[i] = m0 + lrow[i] < p.M ? o : OOB;
+        for (int i = 0; i < 3; ++i) {
+            const int d = w + 8 * i, j = d / 3;
+            sow[i] = (uint32_t)(j * KSTRIDE + 1024 * (d % 3));
+            oobw[i] = bw0 + j < nblk_w ? 0u : OOB;
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int d = w + 8 * i, j = d / 3;
+            sox[i] = d < 12 ? (uint32_t)(j * KSTRIDE + 1024 * (d % 3)) : 0u;
+            oobx[i] = d < 12 && bx0 + j < nblk_x ? 0u : OOB;
         }
     };
     // A group's scales go to ring slot (group & 3): waves 0 and 1 load the 256 sw values (4
@@ -179,8 +235,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
             }
         }
     };
-    // Issue the next K-tile of the stream into stage (g % 3): 6 loads per wave, after the group
-    // scales (even K-tiles) and the tile's bias (first K-tile).
+    // Issue the next K-tile of the stream into stage (g % NST): 5 loads per wave, after the
+    // group scales (even K-tiles) and the tile's bias (first K-tile).
     int ld_kt = 0, ld_g = 0;
     auto issue = [&](int g) {
         if (ld_kt == 0) {
@@ -188,78 +244,114 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
             issue_bias(ld_t);
         }
         if ((ld_kt & 1) == 0) issue_scales(ld_g++, ld_kt >> 1);
-        const int k0 = __builtin_amdgcn_readfirstlane(ld_kt * BK);
+        const int k0 = __builtin_amdgcn_readfirstlane(ld_kt * CHUNK);
         if (++ld_kt == KT) ld_kt = 0;
-        uint8_t *base = smem + (g % NST) * STAGE + w * 1024;
+        uint8_t *base = smem + (g % NST) * STAGE;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + 8 * i * 1024), 16, offw[i], k0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(base + WB + 8 * i * 1024), 16, offx[i], k0, 0, 0);
+        for (int i = 0; i < 3; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + 1024 * (w + 8 * i)), 16, lane16 | oobw[i],
+                                                     k0 + sow[i], 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(base + WB + 1024 * w), 16, lane16 | oobx[0], k0 + sox[0],
+                                                 0, 0);
+        // waves 4..7: token piece w + 8 does not exist; the load is out of range and the zeros
+        // land in the dummy area
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rx, (lds_void *)(w < 4 ? base + WB + 1024 * (w + 8) : smem + DUMMY_OFF), 16, lane16 | oobx[1], k0 + sox[1],
+            0, 0);
     };
 
-    // Fragments: row = wave base + 32*blk + lane%32; sub-step kk (0..3) reads K chunk 2kk + lane/32.
+    // Fragments: weight block bi of the wave is row block 2 wn + bi, token block bj is row block
+    // 2 wm + bj; K-step ks of the K-tile is the piece at ks * 1536 inside the block's chunk.  A
+    // lane's 24 bytes are one 16-byte read (bytes 0..1023 of the piece) and one 8-byte read
+    // (bytes 1024..1535), which land in the operand's 6 consecutive registers.  Each fragment
+    // gets its own address register for the 8-byte read: with a shared one the compiler pairs
+    // the reads of two fragments into one ds_read2 and must then copy the halves apart.
     const int frow = lane & 31, fhalf = lane >> 5;
-    const int arow = (wn * 64 + frow) * BK, brow = WB + (wm * 64 + frow) * BK;
-    const int fpos[4] = {((0 + fhalf) ^ swz(frow)) * 16, ((2 + fhalf) ^ swz(frow)) * 16,
-                         ((4 + fhalf) ^ swz(frow)) * 16, ((6 + fhalf) ^ swz(frow)) * 16};
-    v4i fa[2][2], fb[2][2];
-    auto read_frags = [&](int g, int kk, int buf) {
-        const uint8_t *s0 = smem + (g % NST) * STAGE + fpos[kk];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) fa[buf][b] = *reinterpret_cast<const v4i *>(s0 + arow + 32 * b * BK);
-#pragma unroll
-        for (int b = 0; b < 2; ++b) fb[buf][b] = *reinterpret_cast<const v4i *>(s0 + brow + 32 * b * BK);
+    const int lane8 = 1024 + 8 * lane;
+    v8i fa[2][2], fb[2][2];
+    auto join = [](const v4i &a, const v2i &b) {
+        const v4i bb = __builtin_shufflevector(b, b, 0, 1, -1, -1);
+        return __builtin_shufflevector(a, bb, 0, 1, 2, 3, 4, 5, -1, -1);
     };
-    v16i iacc[2][2];                         // current group (first written with a zero C)
+    auto read_frags = [&](int g, int ks, int buf) {
+        const int so = (g % NST) * STAGE + ks * PIECE;
+        const uint8_t *h = smem + so + lane16;
+        int t[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            // f = 0, 1: weight blocks; 2, 3: token blocks
+            t[f] = lane8 + so + (f < 2 ? (2 * wn + f) * CHUNK : WB + (2 * wm + f - 2) * CHUNK);
+            asm volatile("" : "+v"(t[f]));
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            fa[buf][b] = join(*reinterpret_cast<const v4i *>(h + (2 * wn + b) * CHUNK),
+                              *reinterpret_cast<const v2i *>(smem + t[b]));
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            fb[buf][b] = join(*reinterpret_cast<const v4i *>(h + WB + (2 * wm + b) * CHUNK),
+                              *reinterpret_cast<const v2i *>(smem + t[2 + b]));
+    };
+    v16f gacc[2][2];                         // current group (first written with a zero C)
     v16f facc[2][2];                         // sum over groups (zeroed at each tile's start)
     auto mfmas = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int bi = j >> 1, bj = j & 1;
-            iacc[bi][bj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[buf][bi], fb[buf][bj], iacc[bi][bj], 0, 0, 0);
+            gacc[bi][bj] = mfma_fp6(fa[buf][bi], fb[buf][bj], gacc[bi][bj]);
         }
     };
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
-    // Fold of block (bi, bj) of group with scale slot gidx into facc (zeroed at the tile's
-    // start; a select between "first" and "accumulate" forms would cost the VALU both):
-    // lane holds token m = lane%32 of the block and weight rows n = 8*(v/4) + 4*(lane/32) + v%4.
-    // (16*16 = 256 is in sx / 256.)
-    auto fold_block = [&](int gidx, int bi, int bj) {
+    // Fold of a group into facc (zeroed at the tile's start): facc += gacc * sx[m] * sw[n].
+    // Lane holds token m = lane%32 of block (bi, bj) and weight rows n = 8*(v/4) + 4*(lane/32) + v%4.
+    // The per-output scale product P = sw[n] * sx[m] of each 32x32 block is an outer product,
+    // made by one f16 MFMA with K = 8 of which only k = 0 is non-zero: A row i holds sw of the
+    // block's weight row i, B column j holds sx of its token j, so P lands in the accumulator's
+    // own layout, exact (a product of two fp16 values fits fp32).  The fold is then one FMA per
+    // output, the same fma(acc, sx*sw, facc) as an exact-product reference.  A lane < 32 loads
+    // its k = 0 entry zero-extended (k = 1..3 zero); lanes >= 32 (k = 4..7) read, for A, the
+    // finite scale of lane - 32 and, for B, the zero slot, so every k >= 1 term is 0.
+    const int sw_off = 2 * (wn * 64 + frow);                               // + 64 * bi
+    const int sx_off = lane < 32 ? 2 * BN + 4 * (wm * 64 + frow) : -1;     // + 128 * bj
+    v4h pa[2], pb[2];
+    auto read_scales = [&](int gidx) {
+        const uint8_t *sb = smem + SC_OFF + (gidx & (NSC - 1)) * SC_BYTES;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const uint32_t a = *reinterpret_cast<const uint16_t *>(sb + sw_off + 64 * b);
+            pa[b] = __builtin_bit_cast(v4h, v2u{a, 0u});
+            const uint32_t x = *reinterpret_cast<const uint32_t *>(
+                sx_off >= 0 ? sb + sx_off + 128 * b : smem + ZERO_OFF);
+            pb[b] = __builtin_bit_cast(v4h, v2u{x, 0u});
+        }
+    };
+    auto fold_block = [&](int bi, int bj) {
         if constexpr (E == Epi::Int32) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int s = iacc[bi][bj][v] >> 8;       // exact: every product is 256 * cx * cw
+                const int s = (int)gacc[bi][bj][v];       // exact: an integer below 2^24
                 facc[bi][bj][v] = __int_as_float(__float_as_int(facc[bi][bj][v]) + s);
             }
         } else {
-            const uint16_t *sb = reinterpret_cast<const uint16_t *>(smem + SC_OFF + (gidx & (NSC - 1)) * SC_BYTES);
-            const uint32_t *sxd = reinterpret_cast<const uint32_t *>(sb + BN);          // one per dword
-            const float sxm = f16_to_f32((uint16_t)sxd[wm * 64 + 32 * bj + frow]) * (1.0f / 256.0f);
+            // keep each block's scale product next to its fold (hoisting all four would hold
+            // 64 more registers)
+            v4h a = pa[bi];
+            asm volatile("" : "+v"(a));
+            const v16f pr = __builtin_amdgcn_mfma_f32_32x32x8f16(a, pb[bj], v16f{}, 0, 0, 0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int nl = wn * 64 + 32 * bi + 8 * q + 4 * fhalf;
-                const uint2 s2 = *reinterpret_cast<const uint2 *>(sb + nl);   // 4 fp16 scales
-                const float sw4[4] = {f16_to_f32((uint16_t)(s2.x & 0xffff)), f16_to_f32((uint16_t)(s2.x >> 16)),
-                                      f16_to_f32((uint16_t)(s2.y & 0xffff)), f16_to_f32((uint16_t)(s2.y >> 16))};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int v = 4 * q + e;
-                    facc[bi][bj][v] = __builtin_fmaf((float)iacc[bi][bj][v], sxm * sw4[e], facc[bi][bj][v]);
-                }
-            }
+            for (int v = 0; v < 16; ++v) facc[bi][bj][v] = __builtin_fmaf(gacc[bi][bj][v], pr[v], facc[bi][bj][v]);
         }
     };
-    // First sub-step of a group: fold the previous group (if any) block by block, each right
+    // First K-step of a group: fold the previous group (if any) block by block, each right
     // before the zero-C MFMA that restarts that block.
     auto group_start = [&](bool fold, int gidx) {
+        if (fold && E == Epi::Bf16) read_scales(gidx);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int bi = j >> 1, bj = j & 1;
-            if (fold) fold_block(gidx, bi, bj);
-            iacc[bi][bj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[0][bi], fb[0][bj], v16i{}, 0, 0, 0);
+            if (fold) fold_block(bi, bj);
+            gacc[bi][bj] = mfma_fp6(fa[0][bi], fb[0][bj], v16f{});
             fence();
         }
     };
@@ -317,64 +409,74 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
     };
 
     if (ntiles <= 0) return;
-    constexpr int LPW = 6;                                  // K-tile loads per wave
+    if (threadIdx.x < 4) reinterpret_cast<uint32_t *>(smem + ZERO_OFF)[threadIdx.x] = 0u;   // before the first barrier
+    constexpr int LPW = 5;                                  // K-tile loads per wave
     constexpr int EPI_STORES = E == Epi::Int32 ? 16 : 8;   // stores per wave after an epilogue
+    constexpr int AHEAD = (NST - 2) * LPW;                  // loads younger than K-tile g + 1's
     issue(0);
-    if (total > 1) issue(1);
-    if (total > 2) issue(2);
-    if (total > 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPW));
-    else if (total > 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+#pragma unroll
+    for (int i = 1; i < NST; ++i)
+        if (i < total) issue(i);
+    // K-tile 0 must have landed; every later prologue K-tile may still be in flight
+    {
+        const int later = (total < NST ? total : NST) - 1;
+        if (later >= NST - 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm((NST - 1) * LPW));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
     __syncthreads();
     read_frags(0, 0, 0);
 
-    int g = 0, gidx = 0;                                    // gidx: this stream's group index
+    // End of K-tile g's first K-step: K-tile g+1 must have landed (at most the loads of K-tiles
+    // g+2 .. g+NST-1 and, while the previous tile's epilogue stores are younger than K-tile
+    // g+1's loads, those stores may still be in flight), then every wave has finished reading
+    // stage g % NST, which takes K-tile g+NST; then K-tile g's second K-step.
+    int g = 0;
+    auto tail = [&](int t, int kt) {
+        fence();
+        if (g + NST - 1 < total) {
+            if (t > 0 && kt < NST - 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(AHEAD + EPI_STORES));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(AHEAD));
+        } else {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (g + NST < total) issue(g + NST);
+        if (g + 1 < total) read_frags(g + 1, 0, 0);
+        fence();
+        mfmas(1);
+        fence();
+        ++g;
+    };
+
+    int gidx = 0;                                           // this stream's group index
     for (int t = 0; t < ntiles; ++t) {
-        for (int kt = 0; kt < KT; ++kt, ++g) {
-            if ((kt & 1) == 0) {
-                // first K-tile of a group: restart the int32 blocks (folding the previous group)
-                if (kt == 0) {
 #pragma unroll
-                    for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-                        for (int b = 0; b < 2; ++b) facc[a][b] = v16f{};
-                }
-                group_start(kt > 0, gidx - 1);
-                fence();
-                read_frags(g, 1, 1);
-            } else {
-                read_frags(g, 1, 1);
-                fence();
-                mfmas(0);
-            }
-            fence();
-            read_frags(g, 2, 0);
-            fence();
-            mfmas(1);
-            fence();
-            read_frags(g, 3, 1);
+            for (int b = 0; b < 2; ++b) facc[a][b] = v16f{};
+        // group 0 of the tile: nothing to fold
+        group_start(false, 0);
+        read_frags(g, 1, 1);
+        tail(t, 0);
+        read_frags(g, 1, 1);
+        fence();
+        mfmas(0);
+        tail(t, 1);
+        ++gidx;
+        for (int gi = 1; gi < G; ++gi) {
+            group_start(true, gidx - 1);
+            read_frags(g, 1, 1);
+            tail(t, 2 * gi);
+            read_frags(g, 1, 1);
             fence();
             mfmas(0);
-            fence();
-            // K-tile g+1 must have landed: at most K-tile g+2's loads (and, in a tile's first
-            // two K-tiles, the previous tile's epilogue stores) may still be in flight.
-            if (g + 2 < total) {
-                if (t > 0 && kt < 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW + EPI_STORES));
-                else __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW));
-            } else {
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            if (g + 3 < total) issue(g + 3);
-            if (g + 1 < total) read_frags(g + 1, 0, 0);
-            fence();
-            mfmas(1);
-            fence();
-            if (kt & 1) ++gidx;
+            tail(t, 2 * gi + 1);
+            ++gidx;
         }
         // the tile's last group, then its epilogue
+        if (E == Epi::Bf16) read_scales(gidx - 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fold_block(gidx - 1, j >> 1, j & 1);
+        for (int j = 0; j < 4; ++j) fold_block(j >> 1, j & 1);
         epilogue(t);
     }
 }
@@ -390,25 +492,30 @@ int cu_count()
     return cus;
 }
 
+int64_t row_blocks(int64_t R) { return (R + 31) / 32; }
+
 } // namespace
 
-size_t w4a4_unpacked_bytes(int64_t M, int64_t N, int K) { return (size_t)(M + N) * (size_t)K; }
+size_t w4a4_tiled_bytes(int64_t M, int64_t N, int K)
+{
+    return (size_t)(row_blocks(M) + row_blocks(N)) * (size_t)(K / 64) * PIECE;
+}
 
 hipError_t launch_gemm_w4a4(const uint8_t *xq, const uint8_t *wq, const uint16_t *sx, const uint16_t *sw,
                             const float *bias, void *y, Epi epi, int64_t M, int64_t N, int K, void *ws,
                             hipStream_t stream)
 {
     if (M <= 0 || N <= 0) return hipSuccess;
-    int8_t *xu = static_cast<int8_t *>(ws);
-    int8_t *wu = xu + M * (int64_t)K;
-    // unpack both operands (K/32 16-byte blocks per row)
-    const int64_t nx = M * (K / 32), nw = N * (K / 32);
+    const int64_t px = row_blocks(M) * (K / 64), pw = row_blocks(N) * (K / 64);
+    if (px >= ((int64_t)1 << 31) || pw >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    uint8_t *xt = static_cast<uint8_t *>(ws);
+    uint8_t *wt = xt + px * PIECE;
     const unsigned ugrid = (unsigned)(cu_count() * 8);
-    hipLaunchKernelGGL(unpack_i4_kernel, dim3(ugrid), dim3(256), 0, stream, xq, xu, nx);
-    hipLaunchKernelGGL(unpack_i4_kernel, dim3(ugrid), dim3(256), 0, stream, wq, wu, nw);
+    hipLaunchKernelGGL(tile_fp6_kernel, dim3(ugrid), dim3(256), 0, stream, xq, xt, M, K, (uint32_t)px);
+    hipLaunchKernelGGL(tile_fp6_kernel, dim3(ugrid), dim3(256), 0, stream, wq, wt, N, K, (uint32_t)pw);
     W4Params p;
-    p.xq = xu;
-    p.wq = wu;
+    p.xt = xt;
+    p.wt = wt;
     p.sx = sx;
     p.sw = sw;
     p.bias = bias;

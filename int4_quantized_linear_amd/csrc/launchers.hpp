@@ -26,8 +26,8 @@ hipError_t launch_gemv_i8(const int8_t *xq, const int8_t *wq, const float *sx, c
 
 // W4A4: y = bf16(sum_g acc_g * sx[m,g] * sw[n,g] + bias[n]) with packed int4 operands and
 // fp16 group scales (group = 256), or the unscaled int32 total sum_k cx*cw (scales ignored).
-// `ws` is scratch of w4a4_unpacked_bytes() bytes (16-byte aligned) for the unpacked codes.
-size_t w4a4_unpacked_bytes(int64_t M, int64_t N, int K);
+// `ws` is scratch of w4a4_tiled_bytes() bytes (16-byte aligned) for both operands in FP6 tiles.
+size_t w4a4_tiled_bytes(int64_t M, int64_t N, int K);
 hipError_t launch_gemm_w4a4(const uint8_t *xq, const uint8_t *wq, const uint16_t *sx, const uint16_t *sw,
                             const float *bias, void *y, Epi epi, int64_t M, int64_t N, int K, void *ws,
                             hipStream_t stream);
