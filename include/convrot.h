@@ -122,6 +122,29 @@ int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uin
                         int64_t N, int64_t K, int group, const uint8_t *wq, const uint16_t *w_scale,
                         const float *bias, void *y, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * One-time re-encode of W4A4 weights for the matrix core (the same operation
+ * convrot_linear_w4a4 performs on its weights every call, nvfp4-convrot page, section 五):
+ * wq uint8 [N, K/2] from convrot_prepare_weight(bits = 4) becomes convrot_packed_bytes_w4a4(N, K)
+ * bytes (16-byte aligned) of FP6 E3M2 codes in matrix-core order, 1536 bytes per 32 rows x 64
+ * channels (rows past N are zero).  Every code keeps its value (-8..7 are exact E3M2 values);
+ * the scales stay in w_scale, unchanged.  K % 256 == 0.
+ */
+int convrot_pack_weight_w4a4(const uint8_t *wq, int64_t N, int64_t K, void *w_packed, hipStream_t stream);
+
+/* Size of the W4A4 packed weight buffer (0.75 bytes per code); 0 on invalid arguments. */
+size_t convrot_packed_bytes_w4a4(int64_t N, int64_t K);
+
+/*
+ * convrot_linear_w4a4 with the weights already re-encoded by convrot_pack_weight_w4a4 (w_scale
+ * as before).  Same arguments, checks and result bit for bit; the workspace needs only
+ * convrot_workspace_bytes(M, 0, K, 4) bytes, since no weight codes are re-encoded per call.
+ */
+int convrot_linear_w4a4_packed(const void *x, int x_dtype, const uint8_t *xq, const uint16_t *x_scale, int64_t M,
+                               int64_t N, int64_t K, int group, const void *w_packed, const uint16_t *w_scale,
+                               const float *bias, void *y, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
 /* Largest token count of the W4A8 decode linear. */
 #define CONVROT_W4A8_MAX_M 16
 

@@ -28,6 +28,9 @@ SIGNATURES = {
     "convrot_workspace_bytes": ([I64, I64, I64, I], SZ),
     "convrot_linear": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, P, SZ, P], I),
     "convrot_linear_w4a4": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, P, SZ, P], I),
+    "convrot_pack_weight_w4a4": ([P, I64, I64, P, P], I),
+    "convrot_packed_bytes_w4a4": ([I64, I64], SZ),
+    "convrot_linear_w4a4_packed": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, P, SZ, P], I),
     "convrot_linear_w4a8": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, SZ, P], I),
     "convrot_pack_weight_w4a8": ([P, P, I64, I64, P, P], I),
     "convrot_packed_bytes_w4a8": ([I64, I64], SZ),
@@ -168,6 +171,36 @@ def linear_w4a4(x: torch.Tensor | None, wq: torch.Tensor, w_scale: torch.Tensor,
     ws = _workspace(M, N, K, 4, dev)
     _call("convrot_linear_w4a4", _ptr(x), _dtype_code(x) if x is not None else 0, _ptr(xq), _ptr(x_scale), M, N, K,
           group, _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y), _ptr(ws), ws.numel(), _stream(dev))
+    return y
+
+
+def packed_bytes_w4a4(N: int, K: int) -> int:
+    return int(load().convrot_packed_bytes_w4a4(N, K))
+
+
+def pack_weight_w4a4(wq: torch.Tensor) -> torch.Tensor:
+    """Re-encode INT4 weights (prepare_weight(bits=4): wq uint8 [N, K/2]) once as FP6 codes in
+    matrix-core order (a flat uint8 buffer) for linear_w4a4_packed; the scales are unchanged."""
+    _check_dev(wq)
+    N, Kh = wq.shape
+    K = 2 * Kh
+    out = torch.empty(max(packed_bytes_w4a4(N, K), 16), dtype=torch.uint8, device=wq.device)
+    _call("convrot_pack_weight_w4a4", _ptr(wq), N, K, _ptr(out), _stream(wq.device))
+    return out
+
+
+def linear_w4a4_packed(x: torch.Tensor | None, w_packed: torch.Tensor, w_scale: torch.Tensor,
+                       bias: torch.Tensor | None = None, group: int = 256, xq: torch.Tensor | None = None,
+                       x_scale: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """linear_w4a4 with weights from pack_weight_w4a4 (N = w_scale.shape[1]); same result."""
+    _check_dev(x, w_packed, w_scale, bias, xq, x_scale, out)
+    N = w_scale.shape[1]
+    M, K = x.shape if x is not None else (xq.shape[0], 2 * xq.shape[1])
+    dev = w_packed.device
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = _workspace(M, 0, K, 4, dev)
+    _call("convrot_linear_w4a4_packed", _ptr(x), _dtype_code(x) if x is not None else 0, _ptr(xq), _ptr(x_scale), M,
+          N, K, group, _ptr(w_packed), _ptr(w_scale), _ptr(bias), _ptr(y), _ptr(ws), ws.numel(), _stream(dev))
     return y
 
 

@@ -247,27 +247,31 @@ int convrot_gemm_i8_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N
         "gemm_i8");
 }
 
-int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uint16_t *x_scale, int64_t M,
-                        int64_t N, int64_t K, int group, const uint8_t *wq, const uint16_t *w_scale,
-                        const float *bias, void *y, void *workspace, size_t workspace_bytes, hipStream_t stream)
+} // extern "C"
+
+namespace {
+
+// Shared by convrot_linear_w4a4 (packed INT4 weights, re-encoded on every call) and
+// convrot_linear_w4a4_packed (weights re-encoded once by convrot_pack_weight_w4a4).
+int linear_w4a4(const char *who, const void *x, int x_dtype, const uint8_t *xq, const uint16_t *x_scale, int64_t M,
+                int64_t N, int64_t K, int group, const uint8_t *w, bool w_tiled, const uint16_t *w_scale,
+                const float *bias, void *y, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    const char *who = "convrot_linear_w4a4";
     int rc = check_shape(M, N, K, group, who);
     if (rc) return rc;
     if (group != 256 || K % 256) return fail(CONVROT_ERR_GROUP, "%s: W4A4 needs group 256 and K %% 256 == 0", who);
     if (N % 8) return fail(CONVROT_ERR_SHAPE, "%s: N=%lld must be a multiple of 8", who, (long long)N);
     if (M == 0 || N == 0) return CONVROT_OK;
-    if (!wq || !w_scale || !y) return fail(CONVROT_ERR_NULL, "%s: wq, w_scale and y must be non-NULL", who);
+    if (!w || !w_scale || !y) return fail(CONVROT_ERR_NULL, "%s: the weights, w_scale and y must be non-NULL", who);
     if (!x && (!xq || !x_scale)) return fail(CONVROT_ERR_NULL, "%s: give x, or both xq and x_scale", who);
     if (x && x_dtype != CONVROT_DTYPE_F32 && x_dtype != CONVROT_DTYPE_BF16)
         return fail(CONVROT_ERR_DTYPE, "%s: x_dtype=%d", who, x_dtype);
-    if ((x && !aligned(x, 16)) || (!x && (!aligned(xq, 16) || !aligned(x_scale, 2))) || !aligned(wq, 16) ||
+    if ((x && !aligned(x, 16)) || (!x && (!aligned(xq, 16) || !aligned(x_scale, 2))) || !aligned(w, 16) ||
         !aligned(w_scale, 8) || !aligned(y, 16) || (bias && !aligned(bias, 4)))
         return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer (w_scale needs 8 bytes)", who);
-    const WsLayout L = ws_layout(M, N, K, 4);
+    const WsLayout L = ws_layout(M, w_tiled ? 0 : N, K, 4);
     if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
         return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes", who, L.total);
-    if (M == 0 || N == 0) return CONVROT_OK;
     if ((rc = check_device())) return rc;
     if (x) {
         uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -278,9 +282,50 @@ int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uin
         xq = ws + L.xq;
         x_scale = reinterpret_cast<const uint16_t *>(ws + L.xs);
     }
-    return hip_status(convrot::launch_gemm_w4a4(xq, wq, x_scale, w_scale, bias, y, convrot::Epi::Bf16, M, N, (int)K,
-                                                static_cast<uint8_t *>(workspace) + L.tiles, stream),
+    return hip_status(convrot::launch_gemm_w4a4(xq, w, w_tiled, x_scale, w_scale, bias, y, convrot::Epi::Bf16, M, N,
+                                                (int)K, static_cast<uint8_t *>(workspace) + L.tiles, stream),
                       "gemm_w4a4");
+}
+
+} // namespace
+
+extern "C" {
+
+int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uint16_t *x_scale, int64_t M,
+                        int64_t N, int64_t K, int group, const uint8_t *wq, const uint16_t *w_scale,
+                        const float *bias, void *y, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return linear_w4a4("convrot_linear_w4a4", x, x_dtype, xq, x_scale, M, N, K, group, wq, false, w_scale, bias, y,
+                       workspace, workspace_bytes, stream);
+}
+
+size_t convrot_packed_bytes_w4a4(int64_t N, int64_t K)
+{
+    if (N < 0 || N >= ((int64_t)1 << 31) || K <= 0 || K % 256 || K > CONVROT_MAX_K) return 0;
+    return convrot::w4a4_tiled_bytes(0, N, (int)K);
+}
+
+int convrot_pack_weight_w4a4(const uint8_t *wq, int64_t N, int64_t K, void *w_packed, hipStream_t stream)
+{
+    const char *who = "convrot_pack_weight_w4a4";
+    int rc = check_shape(N, 1, K, 256, who);
+    if (rc) return rc;
+    if (K % 256) return fail(CONVROT_ERR_GROUP, "%s: K=%lld must be a multiple of 256", who, (long long)K);
+    if (N == 0) return CONVROT_OK;
+    if (!wq || !w_packed) return fail(CONVROT_ERR_NULL, "%s: wq and w_packed must be non-NULL", who);
+    if (!aligned(wq, 16) || !aligned(w_packed, 16)) return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
+    if ((rc = check_device())) return rc;
+    return hip_status(convrot::launch_tile_w4a4(wq, N, (int)K, static_cast<uint8_t *>(w_packed), stream), "tile_w4a4");
+}
+
+int convrot_linear_w4a4_packed(const void *x, int x_dtype, const uint8_t *xq, const uint16_t *x_scale, int64_t M,
+                               int64_t N, int64_t K, int group, const void *w_packed, const uint16_t *w_scale,
+                               const float *bias, void *y, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream)
+{
+    return linear_w4a4("convrot_linear_w4a4_packed", x, x_dtype, xq, x_scale, M, N, K, group,
+                       static_cast<const uint8_t *>(w_packed), true, w_scale, bias, y, workspace, workspace_bytes,
+                       stream);
 }
 
 size_t convrot_workspace_bytes_w4a8(int64_t M, int64_t N, int64_t K)
@@ -366,7 +411,7 @@ int convrot_gemm_i4_i32(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t
     if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
         return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes", who, L.total);
     if ((rc = check_device())) return rc;
-    return hip_status(convrot::launch_gemm_w4a4(xq, wq, nullptr, nullptr, nullptr, acc, convrot::Epi::Int32, M, N,
+    return hip_status(convrot::launch_gemm_w4a4(xq, wq, false, nullptr, nullptr, nullptr, acc, convrot::Epi::Int32, M, N,
                                                 (int)K, static_cast<uint8_t *>(workspace) + L.tiles, stream),
                       "gemm_w4a4");
 }

@@ -115,33 +115,42 @@ __device__ __forceinline__ v16f mfma_fp6(const v8i &a, const v8i &b, const v16f 
 }
 
 // ---------------------------------------------------------------------------------------------
-// tile: one thread per (piece, lane): 16 packed bytes (32 codes) in, 24 bytes out.
+// tile: a workgroup re-encodes 32 rows x 256 channels (4 pieces) per step.  Thread t reads the
+// 16 packed bytes (32 codes) of row t/8 at channel chunk t%8, so a wavefront reads 8 whole
+// 128-byte lines, and those 32 codes are exactly what lane (row, chunk%2) of piece (chunk/2)
+// holds: 24 bytes out.  A byte's two nibbles become their two 6-bit codes (12 bits) through a
+// 256-entry table in LDS.  K % 256 == 0.
 
 __global__ void __launch_bounds__(256) tile_fp6_kernel(const uint8_t *src, uint8_t *dst, int64_t R, int K,
-                                                       uint32_t pieces)
+                                                       uint32_t units)
 {
-    const uint32_t KS = (uint32_t)K >> 6;
-    const int64_t n = (int64_t)pieces * 64;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const uint32_t pc = (uint32_t)(i >> 6), l = (uint32_t)i & 63;
-        const uint32_t rb = pc / KS, ks = pc - rb * KS;
-        const int64_t row = 32 * (int64_t)rb + (l & 31);
+    __shared__ uint32_t lut[256];   // byte -> E3M2(low nibble) | E3M2(high nibble) << 6
+    {
+        const uint32_t b = threadIdx.x, lo = b & 15u, hi = b >> 4;
+        const uint32_t clo = (uint32_t)(((lo & 8u) ? E3M2_NEG : E3M2_POS) >> (6 * (lo & 7u))) & 63u;
+        const uint32_t chi = (uint32_t)(((hi & 8u) ? E3M2_NEG : E3M2_POS) >> (6 * (hi & 7u))) & 63u;
+        lut[b] = clo | (chi << 6);
+    }
+    __syncthreads();
+    const uint32_t KS = (uint32_t)K >> 6, KQ = (uint32_t)K >> 8;
+    const uint32_t r = threadIdx.x >> 3, c = threadIdx.x & 7;
+    const uint32_t l = r + 32 * (c & 1);                     // lane of the piece
+    for (uint32_t u = blockIdx.x; u < units; u += gridDim.x) {
+        const uint32_t rb = u / KQ, q = u - rb * KQ;
+        const int64_t row = 32 * (int64_t)rb + r;
         v4u d = {0u, 0u, 0u, 0u};
         if (row < R)
-            d = __builtin_nontemporal_load(
-                reinterpret_cast<const v4u *>(src + row * (K >> 1) + 32 * (int64_t)ks + 16 * (l >> 5)));
+            d = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(src + row * (K >> 1) + 128 * q + 16 * c));
         uint32_t o[6] = {0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int s = 0; s < 32; ++s) {
-            // code s = channel 64 ks + 32 h + s: byte s/2, low nibble for even s
-            const uint32_t v = (d[s >> 3] >> (4 * (s & 7))) & 15u;
-            const uint32_t c = (uint32_t)(((v & 8u) ? E3M2_NEG : E3M2_POS) >> (6 * (v & 7u))) & 63u;
-            const int bit = 6 * s, dw = bit >> 5, off = bit & 31;
-            o[dw] |= c << off;
-            if (off > 26) o[dw + 1] |= c >> (32 - off);
+        for (int b = 0; b < 16; ++b) {
+            // byte b = channels 2b (low nibble) and 2b + 1 of the 32: codes 2b and 2b + 1
+            const uint32_t v = lut[(d[b >> 2] >> (8 * (b & 3))) & 255u];
+            const int bit = 12 * b, dw = bit >> 5, off = bit & 31;
+            o[dw] |= v << off;
+            if (off > 20) o[dw + 1] |= v >> (32 - off);
         }
-        uint8_t *piece = dst + (int64_t)pc * PIECE;
+        uint8_t *piece = dst + ((int64_t)rb * KS + 4 * q + (c >> 1)) * PIECE;
         *reinterpret_cast<v4u *>(piece + 16 * l) = v4u{o[0], o[1], o[2], o[3]};
         *reinterpret_cast<v2u *>(piece + 1024 + 8 * l) = v2u{o[4], o[5]};
     }
@@ -501,18 +510,31 @@ size_t w4a4_tiled_bytes(int64_t M, int64_t N, int K)
     return (size_t)(row_blocks(M) + row_blocks(N)) * (size_t)(K / 64) * PIECE;
 }
 
-hipError_t launch_gemm_w4a4(const uint8_t *xq, const uint8_t *wq, const uint16_t *sx, const uint16_t *sw,
-                            const float *bias, void *y, Epi epi, int64_t M, int64_t N, int K, void *ws,
-                            hipStream_t stream)
+hipError_t launch_tile_w4a4(const uint8_t *q, int64_t R, int K, uint8_t *out, hipStream_t stream)
+{
+    if (R <= 0) return hipSuccess;
+    if (K % 256) return hipErrorInvalidValue;
+    const int64_t units = row_blocks(R) * (K / 256);          // 32 rows x 256 channels each
+    if (units >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    const int64_t grid = units < cu_count() * 8 ? units : cu_count() * 8;
+    hipLaunchKernelGGL(tile_fp6_kernel, dim3((unsigned)grid), dim3(256), 0, stream, q, out, R, K, (uint32_t)units);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4a4(const uint8_t *xq, const uint8_t *wq, bool w_tiled, const uint16_t *sx,
+                            const uint16_t *sw, const float *bias, void *y, Epi epi, int64_t M, int64_t N, int K,
+                            void *ws, hipStream_t stream)
 {
     if (M <= 0 || N <= 0) return hipSuccess;
-    const int64_t px = row_blocks(M) * (K / 64), pw = row_blocks(N) * (K / 64);
-    if (px >= ((int64_t)1 << 31) || pw >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     uint8_t *xt = static_cast<uint8_t *>(ws);
-    uint8_t *wt = xt + px * PIECE;
-    const unsigned ugrid = (unsigned)(cu_count() * 8);
-    hipLaunchKernelGGL(tile_fp6_kernel, dim3(ugrid), dim3(256), 0, stream, xq, xt, M, K, (uint32_t)px);
-    hipLaunchKernelGGL(tile_fp6_kernel, dim3(ugrid), dim3(256), 0, stream, wq, wt, N, K, (uint32_t)pw);
+    hipError_t e = launch_tile_w4a4(xq, M, K, xt, stream);
+    if (e != hipSuccess) return e;
+    const uint8_t *wt = wq;
+    if (!w_tiled) {
+        uint8_t *wt_ws = xt + row_blocks(M) * (K / 64) * PIECE;
+        if ((e = launch_tile_w4a4(wq, N, K, wt_ws, stream)) != hipSuccess) return e;
+        wt = wt_ws;
+    }
     W4Params p;
     p.xt = xt;
     p.wt = wt;

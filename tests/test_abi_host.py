@@ -36,6 +36,7 @@ def lib():
 def test_header_declares_the_boundary():
     fns = header_functions()
     for name in ("convrot_prepare_weight", "convrot_quantize_act", "convrot_linear", "convrot_linear_w4a4",
+                 "convrot_pack_weight_w4a4", "convrot_packed_bytes_w4a4", "convrot_linear_w4a4_packed",
                  "convrot_linear_w4a8", "convrot_pack_weight_w4a8", "convrot_packed_bytes_w4a8",
                  "convrot_workspace_bytes", "convrot_workspace_bytes_w4a8",
                  "convrot_gemm_i8_i32", "convrot_gemm_i4_i32", "convrot_dynamic_group", "convrot_last_error",
@@ -104,6 +105,33 @@ def test_packed_bytes_w4a8(lib):
     # 64-row tiles x 256-channel groups, each 8 KiB of codes + 128 bytes of scales
     for N, K in [(64, 256), (1, 256), (1024, 5120), (1000, 5376), (5120, 25600)]:
         assert pb(N, K) == -(-N // 64) * (K // 256) * (8192 + 128), (N, K)
+
+
+def test_packed_bytes_w4a4(lib):
+    pb = lib.convrot_packed_bytes_w4a4
+    assert pb(-1, 512) == 0 and pb(64, 320) == 0 and pb(64, 0) == 0 and pb(64, 131072 + 256) == 0
+    assert pb(0, 512) == 0
+    # 32-row blocks x 64-channel K-steps of 1536 bytes (0.75 bytes per code, rows padded to 32)
+    for N, K in [(32, 256), (1, 256), (10752, 5376), (1000, 5120), (8, 131072)]:
+        assert pb(N, K) == -(-N // 32) * (K // 64) * 1536, (N, K)
+
+
+def test_packed_w4a4_linear_needs_no_weight_workspace(lib):
+    if _gpu_present():
+        pytest.skip("host-only check (fake device pointers)")
+    M, N, K = 64, 1024, 512
+    small = lib.convrot_workspace_bytes(M, 0, K, 4)
+    assert 0 < small < lib.convrot_workspace_bytes(M, N, K, 4)
+    # the per-call path needs room for the weights' FP6 tiles ...
+    rc = lib.convrot_linear_w4a4(*w4_args(M=M, N=N, K=K, wsb=small))
+    assert rc == ERR["CONVROT_ERR_WORKSPACE"], lib.convrot_last_error().decode()
+    # ... the pre-encoded one passes every argument check with the smaller workspace and stops
+    # only at the missing device (hipGetDevice fails on a host without one)
+    rc = lib.convrot_linear_w4a4_packed(*w4_args(M=M, N=N, K=K, wsb=small))
+    assert rc == ERR["CONVROT_ERR_HIP"], lib.convrot_last_error().decode()
+    assert "hipGetDevice" in lib.convrot_last_error().decode()
+    rc = lib.convrot_linear_w4a4_packed(*w4_args(M=M, N=N, K=K, wsb=small - 1))
+    assert rc == ERR["CONVROT_ERR_WORKSPACE"], lib.convrot_last_error().decode()
 
 
 A = 0x100000          # fake 256-byte aligned device addresses (never dereferenced)
@@ -185,8 +213,22 @@ CASES = [
     ("convrot_linear_w4a4", w4_args(dt=9), "CONVROT_ERR_DTYPE"),
     ("convrot_linear_w4a4", w4_args(sw=C + 2), "CONVROT_ERR_ALIGN"),
     ("convrot_linear_w4a4", w4_args(ws=None), "CONVROT_ERR_WORKSPACE"),
-    # the widened codes live in the workspace even for pre-quantized activations
+    # the FP6 tiles live in the workspace even for pre-quantized activations
     ("convrot_linear_w4a4", w4_args(x=None, xq=A, xs=C, ws=None, wsb=0), "CONVROT_ERR_WORKSPACE"),
+    # W4A4 with pre-encoded weights, and the one-time re-encode
+    ("convrot_linear_w4a4_packed", w4_args(group=128), "CONVROT_ERR_GROUP"),
+    ("convrot_linear_w4a4_packed", w4_args(N=252), "CONVROT_ERR_SHAPE"),
+    ("convrot_linear_w4a4_packed", w4_args(wq=None), "CONVROT_ERR_NULL"),
+    ("convrot_linear_w4a4_packed", w4_args(sw=None), "CONVROT_ERR_NULL"),
+    ("convrot_linear_w4a4_packed", w4_args(wq=B + 8), "CONVROT_ERR_ALIGN"),
+    ("convrot_linear_w4a4_packed", w4_args(x=None, xq=A, xs=C, ws=None, wsb=0), "CONVROT_ERR_WORKSPACE"),
+    ("convrot_pack_weight_w4a4", (A, 64, 320, B, None), "CONVROT_ERR_SHAPE"),
+    ("convrot_pack_weight_w4a4", (A, 64, 100, B, None), "CONVROT_ERR_SHAPE"),
+    ("convrot_pack_weight_w4a4", (A, -1, 512, B, None), "CONVROT_ERR_SHAPE"),
+    ("convrot_pack_weight_w4a4", (None, 64, 512, B, None), "CONVROT_ERR_NULL"),
+    ("convrot_pack_weight_w4a4", (A, 64, 512, None, None), "CONVROT_ERR_NULL"),
+    ("convrot_pack_weight_w4a4", (A + 8, 64, 512, B, None), "CONVROT_ERR_ALIGN"),
+    ("convrot_pack_weight_w4a4", (A, 64, 512, B + 8, None), "CONVROT_ERR_ALIGN"),
     # W4A8 decode linear and its weight re-layout
     ("convrot_linear_w4a8", w48_args(M=17), "CONVROT_ERR_SHAPE"),
     ("convrot_linear_w4a8", w48_args(K=100), "CONVROT_ERR_SHAPE"),
@@ -243,6 +285,9 @@ def test_empty_inputs_are_noops(lib):
     assert lib.convrot_linear_w4a8(None, 1, None, None, 0, 256, 512, 256, None, None, None, None, 0, None) == 0
     assert lib.convrot_linear_w4a8(None, 1, None, None, 5, 0, 512, 256, None, None, None, None, 0, None) == 0
     assert lib.convrot_pack_weight_w4a8(None, None, 0, 512, None, None) == 0
+    assert lib.convrot_pack_weight_w4a4(None, 0, 512, None, None) == 0
+    assert lib.convrot_linear_w4a4_packed(None, 1, None, None, 0, 256, 512, 256, None, None, None, None, None, 0,
+                                          None) == 0
     assert lib.convrot_gemm_i8_i32(None, None, 0, 256, 512, None, None, 0, None) == 0
 
 

@@ -265,7 +265,79 @@ def test_gemm_i4_bit_exact(cr, M, N, K):
     assert np.array_equal(_np(acc), orc.gemm_i32(cx, cw))
 
 
+def test_gemm_i4_every_code_at_max_k(cr):
+    # Rows of one constant code each (all 16 nibbles, -8..7) against the same on the weight side
+    # plus random rows, at the largest K: every code's matrix-core encoding is exercised and the
+    # sums reach 64 * 131072 = 2^23 in magnitude.
+    M, N, K = 16, 40, 131072
+    P.say("gemm_i4_i32 every code M=%d N=%d K=%d" % (M, N, K))
+    rng = np.random.default_rng(16)
+    cx = np.repeat(np.arange(-8, 8, dtype=np.int8)[:, None], K, axis=1)
+    cw = np.concatenate([cx, rng.integers(-8, 8, size=(N - M, K), dtype=np.int8)])
+    acc = cr.gemm_i4_i32(torch.from_numpy(orc.pack_i4(cx)).to(DEV), torch.from_numpy(orc.pack_i4(cw)).to(DEV))
+    torch.cuda.synchronize()
+    ref = orc.gemm_i32(cx, cw)
+    assert ref[0, 0] == 64 * K and ref[0, 15] == -56 * K
+    assert np.array_equal(_np(acc), ref)
+
+
+# FP6 E3M2 (OCP Microscaling Formats v1.0): sign bit 5, exponent bits 2..4 with bias 3, mantissa
+# bits 0..1; exponent 0 is subnormal (m/4 * 2^-2).
+def _e3m2_value(c: np.ndarray) -> np.ndarray:
+    c = c.astype(np.int64)
+    e, m = (c >> 2) & 7, c & 3
+    mag = np.where(e == 0, m / 4.0 * 2.0 ** -2, (1 + m / 4.0) * 2.0 ** (e - 3.0))
+    return np.where(c >> 5 == 1, -mag, mag)
+
+
+def _unpack_w4a4_tiles(buf: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Codes [N, K] from the pre-encoded W4A4 buffer: per 32-row block and 64-channel step a
+    1536-byte piece; lane l = r + 32 h holds row r, channels 64 step + 32 h + s at bit 6 s of
+    bytes 16 l .. 16 l + 15 followed by 1024 + 8 l .. 1024 + 8 l + 7."""
+    RB, KS = -(-N // 32), K // 64
+    pieces = buf[:RB * KS * 1536].reshape(RB, KS, 1536)
+    s24 = np.concatenate([pieces[:, :, :1024].reshape(RB, KS, 64, 16), pieces[:, :, 1024:].reshape(RB, KS, 64, 8)],
+                         axis=3)
+    bits = np.unpackbits(s24, axis=3, bitorder="little").reshape(RB, KS, 64, 32, 6).astype(np.int64)
+    codes = (bits << np.arange(6)).sum(axis=4)                       # [RB, KS, lane, s]
+    vals = _e3m2_value(codes).reshape(RB, KS, 2, 32, 32)             # [RB, KS, h, r, s]
+    out = vals.transpose(0, 3, 1, 2, 4).reshape(RB * 32, K)          # row 32 rb + r, channel 64 ks + 32 h + s
+    assert np.all(out == np.round(out))
+    assert np.all(out[N:] == 0), "rows past N must be zeros"
+    return out[:N].astype(np.int64)
+
+
+@pytest.mark.parametrize("N,K", [(32, 256), (200, 512), (1000, 5376)])
+def test_pack_w4a4_layout(cr, N, K):
+    P.say("pack_weight_w4a4 N=%d K=%d" % (N, K))
+    rng = np.random.default_rng(N + K)
+    cw = rng.integers(-8, 8, size=(N, K), dtype=np.int8)
+    wp = cr.pack_weight_w4a4(torch.from_numpy(orc.pack_i4(cw)).to(DEV))
+    torch.cuda.synchronize()
+    assert wp.numel() == cr.packed_bytes_w4a4(N, K)
+    assert np.array_equal(_unpack_w4a4_tiles(_np(wp), N, K), cw.astype(np.int64))
+
+
 W4_LINEAR_CASES = [(4, 256, 512), (130, 264, 768), (257, 1024, 5376), (12, 1024, 5120)]
+
+
+@pytest.mark.parametrize("M,N,K", W4_LINEAR_CASES)
+def test_linear_w4a4_packed_matches(cr, M, N, K):
+    # the pre-encoded weights give the per-call path's result bit for bit, with x and with xq
+    P.say("linear_w4a4_packed M=%d N=%d K=%d" % (M, N, K))
+    x, w, b = workloads.ragged_case(M, K, N, seed=6)
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    wq, ws = cr.prepare_weight(wd, 256, 4)
+    wp = cr.pack_weight_w4a4(wq)
+    xq, xs = cr.quantize_act(xd, 256, 4)
+    y1 = cr.linear_w4a4(xd, wq, ws, bd)
+    y2 = cr.linear_w4a4_packed(xd, wp, ws, bd)
+    y3 = cr.linear_w4a4_packed(None, wp, ws, bd, xq=xq, x_scale=xs)
+    y4 = cr.linear_w4a4_packed(None, wp, ws, None, xq=xq, x_scale=xs)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+    yown = orc.linear_i4(orc.unpack_i4(_np(xq)), _np(xs).T, orc.unpack_i4(_np(wq)), _np(ws).T, None, 256)
+    P.check_y(_x64(y4), yown, "y (no bias, own codes)", strict_frac=1e-4)
 
 
 @pytest.mark.parametrize("M,N,K", W4_LINEAR_CASES)
