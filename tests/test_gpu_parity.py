@@ -359,6 +359,39 @@ def test_linear_w4a4_parity(cr, M, N, K):
     P.check_y(_x64(y), ref["y"], "y (oracle codes)", strict_frac=2e-2)
 
 
+def test_linear_w4a4_full_size_sampled(cr):
+    """Full 4096 x 5376 x 10752 W4A4 workload, per-call and pre-encoded weights (the bench's
+    serving path); the oracle on 384 sampled token rows x 384 sampled weight rows."""
+    M, K, N = workloads.W4A4_SHAPE["M"], workloads.W4A4_SHAPE["K"], workloads.W4A4_SHAPE["N"]
+    P.say("linear_w4a4 full size M=%d N=%d K=%d" % (M, N, K))
+    x, w, b = workloads.prefill_inputs(M, K, N, cfg=workloads.CFG_W4A4)
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    wq, ws = cr.prepare_weight(wd, 256, 4)
+    del wd
+    xq, xs = cr.quantize_act(xd, 256, 4)
+    y = cr.linear_w4a4(xd, wq, ws, bd)
+    yp = cr.linear_w4a4_packed(None, cr.pack_weight_w4a4(wq), ws, bd, xq=xq, x_scale=xs)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yp)
+    rng = np.random.default_rng(12)
+    mr = np.sort(rng.choice(M, 384, replace=False))
+    nr = np.sort(rng.choice(N, 384, replace=False))
+    ys = _x64(y)[np.ix_(mr, nr)]
+    # scales and codes of the sampled rows
+    cx, sxr, _ = orc.prepare_i4(_x64(x[mr]), 256)
+    cw, swr, _ = orc.prepare_i4(_x64(w[nr]), 256)
+    P.check_scales_f16(_np(xs).T[mr], sxr, "sx16 rows")
+    P.check_scales_f16(_np(ws).T[nr], swr, "sw16 rows")
+    P.check_codes(orc.unpack_i4(_np(xq)[mr]), cx, "x int4 codes", rate=1e-3)
+    P.check_codes(orc.unpack_i4(_np(wq)[nr]), cw, "w int4 codes", rate=1e-3)
+    # exact integer part on the GPU's own codes and scales, then the oracle end to end
+    yown = orc.linear_i4(orc.unpack_i4(_np(xq)[mr]), _np(xs).T[mr], orc.unpack_i4(_np(wq)[nr]), _np(ws).T[nr],
+                         b.numpy()[nr], 256)
+    P.check_y(ys, yown, "sampled y (own codes)", strict_frac=1e-4)
+    ref = orc.linear_w4a4(_x64(x[mr]), _x64(w[nr]), b.numpy()[nr], 256)
+    P.check_y(ys, ref["y"], "sampled y (oracle codes)", strict_frac=2e-2)
+
+
 # ------------------------------------------------------------------ W4A8 (decode, M <= 16)
 
 def _w4a8_case(cr, x, w, b, what):
