@@ -306,55 +306,90 @@ def bench_w4a4(cr, wl, torch, steps, warmup):
 
 def bench_stack(cr, wl, torch, layers: int):
     """All layers' INT8 weights resident; per layer: 4 rotate+quantize of the layer's inputs and
-    the 7 linears on the pre-quantized inputs (q/k/v share one, gate/up share one)."""
+    the 7 linears on the pre-quantized inputs (q/k/v share one, gate/up share one).  Also timed:
+    the same layer with the linears that share an input run as one GEMM over their concatenated
+    weight rows (q|k|v, gate|up).  Row-wise scales make the concatenation's preparation exactly the
+    concatenation of the separate ones, so both schedules compute the same outputs; the 7-linear
+    schedule runs on row slices of the concatenated weights."""
     dev = torch.device("cuda:0")
     st = torch.cuda.current_stream(dev)
     M = wl.STACK_M
     log("stack: preparing %d layers of weights and inputs on the device" % layers)
     t0 = time.perf_counter()
+    kdim = dict(wl.STACK_INPUTS)
+    # fused groups in matrix order: the matrices of a group share their input
+    groups = []
+    for i, (name, K, N) in enumerate(wl.STACK_MATRICES):
+        inp = wl.STACK_INPUT_OF[name]
+        if groups and groups[-1][0] == inp:
+            groups[-1][1].append((i, name, N))
+        else:
+            groups.append((inp, [(i, name, N)]))
     W, X = [], []
     for L in range(layers):
-        mats = {}
-        for i, (name, K, N) in enumerate(wl.STACK_MATRICES):
-            mats[name] = cr.prepare_weight(wl.stack_weight(L, i, N, K, dev), 256, 8)
-        W.append(mats)
+        fused = []
+        for inp, members in groups:
+            K = kdim[inp]
+            NT = sum(N for _, _, N in members)
+            wq = torch.empty((NT, K), dtype=torch.int8, device=dev)
+            sw = torch.empty((NT,), dtype=torch.float32, device=dev)
+            n0 = 0
+            for i, name, N in members:
+                cr._call("convrot_prepare_weight", wl.stack_weight(L, i, N, K, dev).data_ptr(), cr.CONVROT_DTYPE_BF16,
+                         N, K, 256, 8, wq[n0:n0 + N].data_ptr(), sw[n0:n0 + N].data_ptr(), st.cuda_stream)
+                torch.cuda.synchronize()
+                n0 += N
+            fused.append((inp, K, NT, wq, sw, members))
+        W.append(fused)
         X.append({inp: wl.stack_acts(L, j, M, K, dev) for j, (inp, K) in enumerate(wl.STACK_INPUTS)})
     torch.cuda.synchronize()
     log("stack: prepared in %.1f s (%.1f GB of INT8 weights)" % (
-        time.perf_counter() - t0, sum(w[0].numel() for m in W for w in m.values()) / 1e9))
+        time.perf_counter() - t0, sum(f[3].numel() for g in W for f in g) / 1e9))
     xq = {inp: torch.empty((M, K), dtype=torch.int8, device=dev) for inp, K in wl.STACK_INPUTS}
     xs = {inp: torch.empty((M,), dtype=torch.float32, device=dev) for inp, _ in wl.STACK_INPUTS}
-    ys = {name: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for name, _, N in wl.STACK_MATRICES}
-    kdim = dict(wl.STACK_INPUTS)
+    ys = {inp: torch.empty((M, sum(N for _, _, N in members)), dtype=torch.bfloat16, device=dev)
+          for inp, members in groups}
 
-    def layer(L):
+    def layer(L, fuse):
         for inp, K in wl.STACK_INPUTS:
             cr._call("convrot_quantize_act", X[L][inp].data_ptr(), cr.CONVROT_DTYPE_BF16, M, K, 256, 8,
                      xq[inp].data_ptr(), xs[inp].data_ptr(), st.cuda_stream)
-        for name, K, N in wl.STACK_MATRICES:
-            inp = wl.STACK_INPUT_OF[name]
-            assert kdim[inp] == K
-            wq, sw = W[L][name]
-            cr._call("convrot_linear", None, 0, xq[inp].data_ptr(), xs[inp].data_ptr(), M, N, K, 256, wq.data_ptr(),
-                     sw.data_ptr(), None, ys[name].data_ptr(), None, 0, st.cuda_stream)
+        for inp, K, NT, wq, sw, members in W[L]:
+            y = ys[inp]
+            if fuse:
+                cr._call("convrot_linear", None, 0, xq[inp].data_ptr(), xs[inp].data_ptr(), M, NT, K, 256,
+                         wq.data_ptr(), sw.data_ptr(), None, y.data_ptr(), None, 0, st.cuda_stream)
+                continue
+            n0 = 0
+            for _, name, N in members:
+                # the separate linear writes its own [M, N] output (a contiguous block of y)
+                cr._call("convrot_linear", None, 0, xq[inp].data_ptr(), xs[inp].data_ptr(), M, N, K, 256,
+                         wq[n0:n0 + N].data_ptr(), sw[n0:n0 + N].data_ptr(), None, y.view(-1)[M * n0:].data_ptr(),
+                         None, 0, st.cuda_stream)
+                n0 += N
+
+    def timed(fuse):
+        per_pass = []
+        for rep in range(3):                      # pass 0 warms up
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(layers + 1)]
+            ev[0].record(st)
+            for L in range(layers):
+                layer(L, fuse)
+                ev[L + 1].record(st)
+            torch.cuda.synchronize()
+            if rep:
+                per_pass.append([ev[i].elapsed_time(ev[i + 1]) for i in range(layers)])
+        per_layer = [t for p in per_pass for t in p]
+        return statistics.median(per_layer), statistics.median([sum(p) for p in per_pass])
 
     ops = sum(2.0 * M * N * K for _, K, N in wl.STACK_MATRICES)
-    per_pass = []
-    for rep in range(3):                      # pass 0 warms up
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(layers + 1)]
-        ev[0].record(st)
-        for L in range(layers):
-            layer(L)
-            ev[L + 1].record(st)
-        torch.cuda.synchronize()
-        if rep:
-            per_pass.append([ev[i].elapsed_time(ev[i + 1]) for i in range(layers)])
-    per_layer = [t for p in per_pass for t in p]
-    med = statistics.median(per_layer)
-    total = statistics.median([sum(p) for p in per_pass])
+    med, total = timed(False)
+    fmed, ftotal = timed(True)
     res = dict(layers=layers, M=M, ops_per_layer=ops, median_layer_us=med * 1e3,
                median_layer_tops=ops / (med * 1e-3) / 1e12, total_ms=total,
-               frac_int8_peak=ops / (med * 1e-3) / 1e12 / PEAK_INT8_TOPS)
+               frac_int8_peak=ops / (med * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+               fused_median_layer_us=fmed * 1e3, fused_median_layer_tops=ops / (fmed * 1e-3) / 1e12,
+               fused_total_ms=ftotal, fused_groups=[[name for _, name, _ in m] for _, m in groups])
     del W, X
     torch.cuda.empty_cache()
     return res
@@ -513,8 +548,10 @@ def main():
         torch.cuda.empty_cache()
     if args.only in ("all", "stack"):
         res["stack"] = bench_stack(cr, wl, torch, args.stack_layers)
-        log("stack: median layer %.1f us (%.0f TOP/s)" % (res["stack"]["median_layer_us"],
-                                                         res["stack"]["median_layer_tops"]))
+        rs = res["stack"]
+        log("stack: median layer %.1f us (%.0f TOP/s) as 7 linears; %.1f us (%.0f TOP/s) with q|k|v and gate|up "
+            "as one GEMM each" % (rs["median_layer_us"], rs["median_layer_tops"], rs["fused_median_layer_us"],
+                                  rs["fused_median_layer_tops"]))
     cpu = None
     if not args.no_cpu_baseline and args.only in ("all", "prefill"):
         cpu = cpu_baseline(wl, torch)

@@ -221,6 +221,24 @@ def test_linear_prefill_full_size_sampled(cr):
     assert np.array_equal(accg[mr[ii], nr[jj]], orc.gemm_i32_pairs(_np(xq), _np(wq), mr[ii], nr[jj]))
 
 
+def test_linear_concatenated_rows_equal_separate(cr):
+    # Linears sharing an input can run as one GEMM over their concatenated weight rows: row-wise
+    # scales make the concatenation's preparation the concatenation of the separate ones, and
+    # every output is computed the same way, so the results are bit-identical.
+    M, K = 300, 1024
+    x = workloads.heavy_tailed_acts(M, K, cfg=97, layer=0).to(DEV)
+    parts = [workloads.gaussian_weights(N, K, cfg=97 + i).to(DEV) for i, N in enumerate((512, 128, 128))]
+    xq, xs = cr.quantize_act(x, 256, 8)
+    sep = []
+    for w in parts:
+        wq, ws = cr.prepare_weight(w, 256, 8)
+        sep.append(cr.linear(None, wq, ws, xq=xq, x_scale=xs))
+    wq, ws = cr.prepare_weight(torch.cat(parts), 256, 8)
+    fused = cr.linear(None, wq, ws, xq=xq, x_scale=xs)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, torch.cat(sep, dim=1))
+
+
 def test_linear_empty_and_repeat(cr):
     w = workloads.gaussian_weights(64, 256, cfg=98).to(DEV)
     wq, ws = cr.prepare_weight(w, 256, 8)
