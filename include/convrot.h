@@ -14,7 +14,7 @@
  *   R       = blockdiag(H_g / sqrt(g), ...) along K, H_g the Sylvester Hadamard matrix
  *             (H[i][j] = (-1)^popcount(i & j)), g a power of two, groups contiguous along K.
  *   INT8:   s = max|v R| / 127 per row (fp32),  q = rint(v R / s) in [-127, 127]
- *   INT4:   s = max|v R over a 256-group| / 7 per (row, group) (fp16), c = rint(v R / s) in [-7, 7]
+ *   INT4:   s = max|v R over a g-group| / 7 per (row, group) (fp16), c = rint(v R / s) in [-7, 7]
  *   linear: y[m,n] = bf16( sum_k xq[m,k] wq[n,k] * sx[m] * sw[n] + bias[n] )          (INT8)
  *           y[m,n] = bf16( sum_j (sum_{k in group j} cx cw) * sx[m,j] * sw[n,j] + bias[n] ) (W4A4)
  *   Because R is orthogonal, (x R)(w R)^T = x w^T, so the integer product of rotated codes
@@ -49,7 +49,7 @@ typedef enum convrot_status {
     CONVROT_OK = 0,
     CONVROT_ERR_NULL = 1,      /* a required pointer is NULL                                   */
     CONVROT_ERR_SHAPE = 2,     /* M, N or K out of range, K % 64 != 0, or K % group != 0         */
-    CONVROT_ERR_GROUP = 3,     /* group not a power of two in [1, 256] (INT4 requires 256)       */
+    CONVROT_ERR_GROUP = 3,     /* group not a power of two in [1, 256] (INT4: 256 or 128)        */
     CONVROT_ERR_ALIGN = 4,     /* a pointer violates the alignment rules above                   */
     CONVROT_ERR_DTYPE = 5,     /* unknown dtype code                                             */
     CONVROT_ERR_BITS = 6,      /* bits is not 8 or 4                                             */
@@ -69,14 +69,16 @@ enum { CONVROT_DTYPE_F32 = 0, CONVROT_DTYPE_BF16 = 1 };
  *   w        [N, K] fp32 or bf16 (w_dtype)
  *   bits 8:  wq int8 [N, K];        w_scale fp32 [N]
  *   bits 4:  wq uint8 [N, K/2] (two codes per byte, even k in the low nibble);
- *            w_scale fp16 [K/256, N] (group-major: scale of row n, group j at j*N + n); group 256.
+ *            w_scale fp16 [K/group, N] (group-major: scale of row n, group j at j*N + n); the
+ *            scale group is the rotation group, 256 or 128 (the dynamic group of a width that 256
+ *            does not divide).
  */
 int convrot_prepare_weight(const void *w, int w_dtype, int64_t N, int64_t K, int group, int bits, void *wq,
                            void *w_scale, hipStream_t stream);
 
 /*
  * Online activation quantization: rotate each token row by the same R and quantize it
- * dynamically (one scale per token for INT8, per (token, 256-group) for INT4).  Same layouts as
+ * dynamically (one scale per token for INT8, per (token, group) for INT4).  Same layouts as
  * convrot_prepare_weight with M rows.  Exposed so one quantized input can feed several linears
  * (for example q/k/v or gate/up projections that share an input).
  */
@@ -110,12 +112,14 @@ int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_
 
 /*
  * W4A4 ConvRot linear (nvfp4-convrot page, section 五): both operands rotated, INT4 per
- * (row, 256-group) with fp16 scales, per-group integer dot products scaled and summed in fp32.
+ * (row, group) with fp16 scales, per-group integer dot products scaled and summed in fp32.
  *   x bf16/fp32 [M, K] quantized into the workspace, or x = NULL and the caller's
- *   xq uint8 [M, K/2] / x_scale fp16 [K/256, M] from convrot_quantize_act(bits = 4).
+ *   xq uint8 [M, K/2] / x_scale fp16 [K/group, M] from convrot_quantize_act(bits = 4).
  *   The workspace (convrot_workspace_bytes(M, N, K, 4)) is required in both cases.
- *   wq uint8 [N, K/2], w_scale fp16 [K/256, N] from convrot_prepare_weight(bits = 4).
- *   group must be 256, K % 256 == 0, N % 8 == 0.  bias fp32 [N] or NULL; y bf16 [M, N].
+ *   wq uint8 [N, K/2], w_scale fp16 [K/group, N] from convrot_prepare_weight(bits = 4).
+ *   group 256, or 128 for a width 256 does not divide (section 四, detail 3, dynamic group; the
+ *   same group as the operands were quantized with); K % group == 0, K >= 256, N % 8 == 0.
+ *   bias fp32 [N] or NULL; y bf16 [M, N].
  *   w_scale must be 8-byte aligned (the kernel reads 4 scales at a time).
  */
 int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uint16_t *x_scale, int64_t M,
@@ -128,7 +132,7 @@ int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uin
  * wq uint8 [N, K/2] from convrot_prepare_weight(bits = 4) becomes convrot_packed_bytes_w4a4(N, K)
  * bytes (16-byte aligned) of FP6 E3M2 codes in matrix-core order, 1536 bytes per 32 rows x 64
  * channels (rows past N are zero).  Every code keeps its value (-8..7 are exact E3M2 values);
- * the scales stay in w_scale, unchanged.  K % 256 == 0.
+ * the scales stay in w_scale, unchanged.  K % 128 == 0.
  */
 int convrot_pack_weight_w4a4(const uint8_t *wq, int64_t N, int64_t K, void *w_packed, hipStream_t stream);
 
@@ -170,7 +174,8 @@ int convrot_linear_w4a8(const void *x, int x_dtype, const int8_t *xq, const floa
 
 /*
  * Offline re-layout of INT4 weights for convrot_linear_w4a8: wq uint8 [N, K/2] and w_scale fp16
- * [K/256, N] from convrot_prepare_weight(bits = 4) go into one buffer of
+ * [K/256, N] from convrot_prepare_weight(bits = 4, group = 256; the decode kernel reads one scale
+ * per 256 channels, so weights prepared with group 128 must not be passed) go into one buffer of
  * convrot_packed_bytes_w4a8(N, K) bytes (16-byte aligned), ordered the way the decode kernel
  * streams them: per 64-row tile and 256-channel group, the tile's codes (8 KiB, in MFMA operand
  * order) followed by its 64 scales; rows past N are zero.  The codes and scales are copied
@@ -206,7 +211,8 @@ int convrot_gemm_i4_i32(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t
  * detail 3: --dynamic-convrot with --convrot-group-size 256).  Returns the largest power of two
  * <= max_group dividing K (256 for K = 5120 or 5376, 128 for the K = 2688 adaln projection), or
  * 0 when K <= 0 or max_group is not a power of two in [1, 256].  Pass the result as `group` to
- * convrot_prepare_weight, convrot_quantize_act and convrot_linear (the INT4 paths need 256).
+ * convrot_prepare_weight, convrot_quantize_act, convrot_linear and, for 128 or 256,
+ * convrot_linear_w4a4 (the W4A8 decode path needs 256).
  */
 int convrot_dynamic_group(int64_t K, int max_group);
 

@@ -126,14 +126,16 @@ def _quant(name: str, v: torch.Tensor, group: int, bits: int):
         s = torch.empty((R,), dtype=torch.float32, device=v.device)
     else:
         q = torch.empty((R, K // 2), dtype=torch.uint8, device=v.device)
-        s = torch.empty((K // 256, R), dtype=torch.float16, device=v.device)
+        # one fp16 scale per (group, row); an invalid group is rejected by the library before any write
+        ngroups = K // group if group > 0 and K % group == 0 else 1
+        s = torch.empty((ngroups, R), dtype=torch.float16, device=v.device)
     _call(name, _ptr(v), _dtype_code(v), R, K, group, bits, _ptr(q), _ptr(s), _stream(v.device))
     return q, s
 
 
 def prepare_weight(w: torch.Tensor, group: int = 256, bits: int = 8):
     """Rotate + quantize a weight [N, K] -> (wq, w_scale).  bits 8: int8 [N,K], fp32 [N];
-    bits 4: uint8 [N,K/2] packed, fp16 [K/256, N]."""
+    bits 4: uint8 [N,K/2] packed, fp16 [K/group, N] (group 256 or 128)."""
     return _quant("convrot_prepare_weight", w, group, bits)
 
 

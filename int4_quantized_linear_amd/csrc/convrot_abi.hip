@@ -76,7 +76,8 @@ int hip_status(hipError_t e, const char *what)
 
 // Workspace layout, each region 256-byte aligned; all of it is scratch (no initial contents):
 //   bits 8: [xq int8 M*K][x_scale fp32 M]
-//   bits 4: [xq packed M*K/2][x_scale fp16 (K/256)*M][FP6 tiles of both operands]
+//   bits 4: [xq packed M*K/2][x_scale fp16 (K/128)*M, enough for either INT4 group][FP6 tiles of
+//           both operands]
 struct WsLayout {
     size_t xq = 0, xs = 0, tiles = 0, total = 0;
 };
@@ -94,7 +95,7 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int bits)
         L.xq = off;
         off += round256((size_t)(M * K / 2));
         L.xs = off;
-        off += round256((size_t)(M * (K / 256) * 2));
+        off += round256((size_t)(M * ((K + 127) / 128) * 2));
         L.tiles = off;
         off += round256(convrot::w4a4_tiled_bytes(M, N, (int)K));
     }
@@ -125,8 +126,8 @@ int quantize_common(const void *x, int dtype, int64_t R, int64_t K, int group, i
     if (bits != 8 && bits != 4) return fail(CONVROT_ERR_BITS, "%s: bits=%d", who, bits);
     int rc = check_shape(R, 1, K, group, who);
     if (rc) return rc;
-    if (bits == 4 && (group != 256 || K % 256))
-        return fail(CONVROT_ERR_GROUP, "%s: INT4 needs group 256 and K %% 256 == 0 (group=%d, K=%lld)", who, group, (long long)K);
+    if (bits == 4 && group != 256 && group != 128)
+        return fail(CONVROT_ERR_GROUP, "%s: INT4 needs group 256 or 128 (group=%d, K=%lld)", who, group, (long long)K);
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, bits == 8 ? 4 : 2))
         return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
     if (R == 0) return CONVROT_OK;
@@ -259,7 +260,10 @@ int linear_w4a4(const char *who, const void *x, int x_dtype, const uint8_t *xq, 
 {
     int rc = check_shape(M, N, K, group, who);
     if (rc) return rc;
-    if (group != 256 || K % 256) return fail(CONVROT_ERR_GROUP, "%s: W4A4 needs group 256 and K %% 256 == 0", who);
+    if ((group != 256 && group != 128) || K % group)
+        return fail(CONVROT_ERR_GROUP, "%s: W4A4 needs group 256 or 128 dividing K (group=%d, K=%lld)", who, group,
+                    (long long)K);
+    if (K < 256) return fail(CONVROT_ERR_SHAPE, "%s: K=%lld; W4A4 needs K >= 256", who, (long long)K);
     if (N % 8) return fail(CONVROT_ERR_SHAPE, "%s: N=%lld must be a multiple of 8", who, (long long)N);
     if (M == 0 || N == 0) return CONVROT_OK;
     if (!w || !w_scale || !y) return fail(CONVROT_ERR_NULL, "%s: the weights, w_scale and y must be non-NULL", who);
@@ -275,7 +279,7 @@ int linear_w4a4(const char *who, const void *x, int x_dtype, const uint8_t *xq, 
     if ((rc = check_device())) return rc;
     if (x) {
         uint8_t *ws = static_cast<uint8_t *>(workspace);
-        rc = hip_status(convrot::launch_rotate_quant(x, x_dtype == CONVROT_DTYPE_F32, M, (int)K, 8, 4, ws + L.xq,
+        rc = hip_status(convrot::launch_rotate_quant(x, x_dtype == CONVROT_DTYPE_F32, M, (int)K, log2i(group), 4, ws + L.xq,
                                                      ws + L.xs, stream),
                         "rotate_quant");
         if (rc) return rc;
@@ -283,7 +287,7 @@ int linear_w4a4(const char *who, const void *x, int x_dtype, const uint8_t *xq, 
         x_scale = reinterpret_cast<const uint16_t *>(ws + L.xs);
     }
     return hip_status(convrot::launch_gemm_w4a4(xq, w, w_tiled, x_scale, w_scale, bias, y, convrot::Epi::Bf16, M, N,
-                                                (int)K, static_cast<uint8_t *>(workspace) + L.tiles, stream),
+                                                (int)K, group, static_cast<uint8_t *>(workspace) + L.tiles, stream),
                       "gemm_w4a4");
 }
 
@@ -301,16 +305,16 @@ int convrot_linear_w4a4(const void *x, int x_dtype, const uint8_t *xq, const uin
 
 size_t convrot_packed_bytes_w4a4(int64_t N, int64_t K)
 {
-    if (N < 0 || N >= ((int64_t)1 << 31) || K <= 0 || K % 256 || K > CONVROT_MAX_K) return 0;
+    if (N < 0 || N >= ((int64_t)1 << 31) || K <= 0 || K % 128 || K > CONVROT_MAX_K) return 0;
     return convrot::w4a4_tiled_bytes(0, N, (int)K);
 }
 
 int convrot_pack_weight_w4a4(const uint8_t *wq, int64_t N, int64_t K, void *w_packed, hipStream_t stream)
 {
     const char *who = "convrot_pack_weight_w4a4";
-    int rc = check_shape(N, 1, K, 256, who);
+    int rc = check_shape(N, 1, K, 128, who);
     if (rc) return rc;
-    if (K % 256) return fail(CONVROT_ERR_GROUP, "%s: K=%lld must be a multiple of 256", who, (long long)K);
+    if (K % 128) return fail(CONVROT_ERR_GROUP, "%s: K=%lld must be a multiple of 128", who, (long long)K);
     if (N == 0) return CONVROT_OK;
     if (!wq || !w_packed) return fail(CONVROT_ERR_NULL, "%s: wq and w_packed must be non-NULL", who);
     if (!aligned(wq, 16) || !aligned(w_packed, 16)) return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
@@ -386,7 +390,7 @@ int convrot_linear_w4a8(const void *x, int x_dtype, const int8_t *xq, const floa
     if (x) {
         int8_t *qx = reinterpret_cast<int8_t *>(ws + L.xq);
         float *sx = reinterpret_cast<float *>(ws + L.xs);
-        rc = hip_status(convrot::launch_rotate_quant(x, x_dtype == CONVROT_DTYPE_F32, M, (int)K, 8, 8, qx, sx, stream),
+        rc = hip_status(convrot::launch_rotate_quant(x, x_dtype == CONVROT_DTYPE_F32, M, (int)K, log2i(group), 8, qx, sx, stream),
                         "rotate_quant");
         if (rc) return rc;
         xq = qx;
@@ -412,7 +416,7 @@ int convrot_gemm_i4_i32(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t
         return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes", who, L.total);
     if ((rc = check_device())) return rc;
     return hip_status(convrot::launch_gemm_w4a4(xq, wq, false, nullptr, nullptr, nullptr, acc, convrot::Epi::Int32, M, N,
-                                                (int)K, static_cast<uint8_t *>(workspace) + L.tiles, stream),
+                                                (int)K, 256, static_cast<uint8_t *>(workspace) + L.tiles, stream),
                       "gemm_w4a4");
 }
 

@@ -51,7 +51,7 @@ constexpr int DUMMY_OFF = NST * STAGE;            // 1 KiB target of the padding
 constexpr int SC_OFF = DUMMY_OFF + 1024;
 // One group's scales: sw as packed fp16 (512 B), then sx with one fp16 per dword (512 B).
 constexpr int SC_BYTES = 2 * BN + 4 * BM;
-constexpr int NSC = 4;                            // group-scale ring
+constexpr int NSC = 8;                            // group-scale ring (>= NST + 2 groups of one K-tile)
 constexpr int BIAS_OFF = SC_OFF + NSC * SC_BYTES;
 constexpr int NBIAS = 4;                          // per-tile bias ring (fp32)
 constexpr int ZERO_OFF = BIAS_OFF + NBIAS * BN * 4; // 16 zero bytes
@@ -119,7 +119,8 @@ __device__ __forceinline__ v16f mfma_fp6(const v8i &a, const v8i &b, const v16f 
 // 16 packed bytes (32 codes) of row t/8 at channel chunk t%8, so a wavefront reads 8 whole
 // 128-byte lines, and those 32 codes are exactly what lane (row, chunk%2) of piece (chunk/2)
 // holds: 24 bytes out.  A byte's two nibbles become their two 6-bit codes (12 bits) through a
-// 256-entry table in LDS.  K % 256 == 0.
+// 256-entry table in LDS.  K % 128 == 0: with K % 256 == 128 a row block's last step has only
+// 2 pieces, and the threads of the other two do nothing.
 
 __global__ void __launch_bounds__(256) tile_fp6_kernel(const uint8_t *src, uint8_t *dst, int64_t R, int K,
                                                        uint32_t units)
@@ -132,11 +133,13 @@ __global__ void __launch_bounds__(256) tile_fp6_kernel(const uint8_t *src, uint8
         lut[b] = clo | (chi << 6);
     }
     __syncthreads();
-    const uint32_t KS = (uint32_t)K >> 6, KQ = (uint32_t)K >> 8;
+    const uint32_t KS = (uint32_t)K >> 6, KQ = ((uint32_t)K + 255) >> 8;
     const uint32_t r = threadIdx.x >> 3, c = threadIdx.x & 7;
     const uint32_t l = r + 32 * (c & 1);                     // lane of the piece
     for (uint32_t u = blockIdx.x; u < units; u += gridDim.x) {
         const uint32_t rb = u / KQ, q = u - rb * KQ;
+        const uint32_t ks = 4 * q + (c >> 1);                   // K-step of this thread's piece
+        if (ks >= KS) continue;                                  // past K (K % 256 == 128)
         const int64_t row = 32 * (int64_t)rb + r;
         v4u d = {0u, 0u, 0u, 0u};
         if (row < R)
@@ -150,7 +153,7 @@ __global__ void __launch_bounds__(256) tile_fp6_kernel(const uint8_t *src, uint8
             o[dw] |= v << off;
             if (off > 20) o[dw + 1] |= v >> (32 - off);
         }
-        uint8_t *piece = dst + ((int64_t)rb * KS + 4 * q + (c >> 1)) * PIECE;
+        uint8_t *piece = dst + ((int64_t)rb * KS + ks) * PIECE;
         *reinterpret_cast<v4u *>(piece + 16 * l) = v4u{o[0], o[1], o[2], o[3]};
         *reinterpret_cast<v2u *>(piece + 1024 + 8 * l) = v2u{o[4], o[5]};
     }
@@ -158,7 +161,8 @@ __global__ void __launch_bounds__(256) tile_fp6_kernel(const uint8_t *src, uint8
 
 // ---------------------------------------------------------------------------------------------
 
-template <Epi E>
+// GKT: K-tiles per scale group (2 for 256-channel groups, 1 for 128-channel ones).
+template <Epi E, int GKT>
 __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
@@ -166,8 +170,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wn = w & 3, wm = w >> 2;         // wn: 64-row quarter of N, wm: 64-row half of M
     const int K = p.K;
-    const int KT = K / BK;                     // even: K % 256 == 0
-    const int G = K / 256;
+    const int KT = K / BK;                     // a multiple of GKT
+    const int G = KT / GKT;
     const int KSTRIDE = (K / 64) * PIECE;      // bytes between consecutive row blocks
     const int T = p.tiles_m * p.tiles_n;
     const int ntiles = (T - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
@@ -206,7 +210,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
             oobx[i] = d < 12 && bx0 + j < nblk_x ? 0u : OOB;
         }
     };
-    // A group's scales go to ring slot (group & 3): waves 0 and 1 load the 256 sw values (4
+    // A group's scales go to ring slot (group & 7): waves 0 and 1 load the 256 sw values (4
     // bytes = 2 fp16 per lane; N % 8 == 0, so no dword straddles the end of the tile's rows);
     // waves 2 and 3 load the 128 sx values with 2-byte loads, which land zero-extended one per
     // dword, so a tile with an odd number of valid tokens still gets its last scale (a 4-byte
@@ -245,14 +249,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
         }
     };
     // Issue the next K-tile of the stream into stage (g % NST): 5 loads per wave, after the
-    // group scales (even K-tiles) and the tile's bias (first K-tile).
+    // group scales (a group's first K-tile) and the tile's bias (first K-tile).
     int ld_kt = 0, ld_g = 0;
     auto issue = [&](int g) {
         if (ld_kt == 0) {
             set_load_tile(ld_t + 1);
             issue_bias(ld_t);
         }
-        if ((ld_kt & 1) == 0) issue_scales(ld_g++, ld_kt >> 1);
+        if (ld_kt % GKT == 0) issue_scales(ld_g++, ld_kt / GKT);
         const int k0 = __builtin_amdgcn_readfirstlane(ld_kt * CHUNK);
         if (++ld_kt == KT) ld_kt = 0;
         uint8_t *base = smem + (g % NST) * STAGE;
@@ -321,10 +325,13 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
     // output, the same fma(acc, sx*sw, facc) as an exact-product reference.  A lane < 32 loads
     // its k = 0 entry zero-extended (k = 1..3 zero); lanes >= 32 (k = 4..7) read, for A, the
     // finite scale of lane - 32 and, for B, the zero slot, so every k >= 1 term is 0.
-    const int sw_off = 2 * (wn * 64 + frow);                               // + 64 * bi
-    const int sx_off = lane < 32 ? 2 * BN + 4 * (wm * 64 + frow) : -1;     // + 128 * bj
     v4h pa[2], pb[2];
     auto read_scales = [&](int gidx) {
+        // offsets formed here from the lane id (short-lived registers)
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        const int sw_off = 2 * (wn * 64 + (l & 31));                                 // + 64 * bi
+        const int sx_off = l < 32 ? 2 * BN + 4 * (wm * 64 + (l & 31)) : -1;          // + 128 * bj
         const uint8_t *sb = smem + SC_OFF + (gidx & (NSC - 1)) * SC_BYTES;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -467,19 +474,23 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
         group_start(false, 0);
         read_frags(g, 1, 1);
         tail(t, 0);
-        read_frags(g, 1, 1);
-        fence();
-        mfmas(0);
-        tail(t, 1);
+        if constexpr (GKT == 2) {
+            read_frags(g, 1, 1);
+            fence();
+            mfmas(0);
+            tail(t, 1);
+        }
         ++gidx;
         for (int gi = 1; gi < G; ++gi) {
             group_start(true, gidx - 1);
             read_frags(g, 1, 1);
-            tail(t, 2 * gi);
-            read_frags(g, 1, 1);
-            fence();
-            mfmas(0);
-            tail(t, 2 * gi + 1);
+            tail(t, GKT * gi);
+            if constexpr (GKT == 2) {
+                read_frags(g, 1, 1);
+                fence();
+                mfmas(0);
+                tail(t, 2 * gi + 1);
+            }
             ++gidx;
         }
         // the tile's last group, then its epilogue
@@ -513,8 +524,8 @@ size_t w4a4_tiled_bytes(int64_t M, int64_t N, int K)
 hipError_t launch_tile_w4a4(const uint8_t *q, int64_t R, int K, uint8_t *out, hipStream_t stream)
 {
     if (R <= 0) return hipSuccess;
-    if (K % 256) return hipErrorInvalidValue;
-    const int64_t units = row_blocks(R) * (K / 256);          // 32 rows x 256 channels each
+    if (K % 128) return hipErrorInvalidValue;
+    const int64_t units = row_blocks(R) * ((K + 255) / 256);  // 32 rows x 256 channels each
     if (units >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const int64_t grid = units < cu_count() * 8 ? units : cu_count() * 8;
     hipLaunchKernelGGL(tile_fp6_kernel, dim3((unsigned)grid), dim3(256), 0, stream, q, out, R, K, (uint32_t)units);
@@ -523,9 +534,12 @@ hipError_t launch_tile_w4a4(const uint8_t *q, int64_t R, int K, uint8_t *out, hi
 
 hipError_t launch_gemm_w4a4(const uint8_t *xq, const uint8_t *wq, bool w_tiled, const uint16_t *sx,
                             const uint16_t *sw, const float *bias, void *y, Epi epi, int64_t M, int64_t N, int K,
-                            void *ws, hipStream_t stream)
+                            int group, void *ws, hipStream_t stream)
 {
     if (M <= 0 || N <= 0) return hipSuccess;
+    // scale groups of 2 K-tiles (256 channels) or 1 (128); at least 2 K-tiles (bias ring)
+    const int gkt = group / BK;
+    if ((gkt != 1 && gkt != 2) || K % group || K < 2 * BK) return hipErrorInvalidValue;
     uint8_t *xt = static_cast<uint8_t *>(ws);
     hipError_t e = launch_tile_w4a4(xq, M, K, xt, stream);
     if (e != hipSuccess) return e;
@@ -550,10 +564,15 @@ hipError_t launch_gemm_w4a4(const uint8_t *xq, const uint8_t *wq, bool w_tiled, 
     const int T = p.tiles_m * p.tiles_n;
     int grid = cu_count();
     if (T < grid) grid = (T + 7) & ~7;
-    if (epi == Epi::Int32)
-        hipLaunchKernelGGL(gemm_w4a4_kernel<Epi::Int32>, dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
-    else
-        hipLaunchKernelGGL(gemm_w4a4_kernel<Epi::Bf16>, dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
+    if (epi == Epi::Int32) {
+        // the integer sums do not depend on the scale grouping
+        if (gkt == 2) hipLaunchKernelGGL((gemm_w4a4_kernel<Epi::Int32, 2>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
+        else hipLaunchKernelGGL((gemm_w4a4_kernel<Epi::Int32, 1>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
+    } else if (gkt == 2) {
+        hipLaunchKernelGGL((gemm_w4a4_kernel<Epi::Bf16, 2>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((gemm_w4a4_kernel<Epi::Bf16, 1>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

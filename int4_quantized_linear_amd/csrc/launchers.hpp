@@ -25,16 +25,17 @@ hipError_t launch_gemv_i8(const int8_t *xq, const int8_t *wq, const float *sx, c
                           void *y, Epi epi, int64_t M, int64_t N, int K, hipStream_t stream);
 
 // W4A4: y = bf16(sum_g acc_g * sx[m,g] * sw[n,g] + bias[n]) with packed int4 operands and
-// fp16 group scales (group = 256), or the unscaled int32 total sum_k cx*cw (scales ignored).
+// fp16 group scales (group = 256 or 128, K % group == 0, K >= 256), or the unscaled int32 total
+// sum_k cx*cw (scales ignored).
 // Both operands run through the FP6 tiles of launch_tile_w4a4; the weights are re-encoded
 // into `ws` on every call, unless w_tiled says wq already holds their tiles.  `ws` is scratch
 // of w4a4_tiled_bytes(M, w_tiled ? 0 : N, K) bytes (16-byte aligned).
 size_t w4a4_tiled_bytes(int64_t M, int64_t N, int K);
-// Packed int4 rows [R, K/2] -> FP6 tiles (w4a4_tiled_bytes(R, 0, K) bytes), K % 256 == 0.
+// Packed int4 rows [R, K/2] -> FP6 tiles (w4a4_tiled_bytes(R, 0, K) bytes), K % 128 == 0.
 hipError_t launch_tile_w4a4(const uint8_t *q, int64_t R, int K, uint8_t *out, hipStream_t stream);
 hipError_t launch_gemm_w4a4(const uint8_t *xq, const uint8_t *wq, bool w_tiled, const uint16_t *sx,
                             const uint16_t *sw, const float *bias, void *y, Epi epi, int64_t M, int64_t N, int K,
-                            void *ws, hipStream_t stream);
+                            int group, void *ws, hipStream_t stream);
 
 // W4A8 decode linear (M <= 16): y = bf16(sx[m] * sum_g sw[g,n] * (qx . cw over group g) + bias[n])
 // with INT8 tokens and the weights in the W4A8 block layout (codes and fp16 group scales), made

@@ -7,8 +7,9 @@
 // quantizes to 4 bits with RTN).
 //   BITS = 8: one fp32 scale per row = max|rotated row| / 127 (weights: per output channel,
 //             the row-wise scaling of the converter; activations: per token, at run time).
-//   BITS = 4: one fp16 scale per (row, 256-channel group) = max|group| / 7, stored group-major
-//             ([K/256, rows]); two codes per byte with the even channel in the low nibble.
+//   BITS = 4: one fp16 scale per (row, g-channel group) = max|group| / 7 with g = 256, or 128
+//             for a width 256 does not divide (section 四, detail 3, dynamic group), stored
+//             group-major ([K/g, rows]); two codes per byte with the even channel in the low nibble.
 // The same kernel prepares weights (rows = N) and quantizes activations (rows = M).
 //
 // Data layout in registers.  A row is cut into "slots" of 256 consecutive channels.  Inside a
@@ -191,25 +192,30 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
             }
         }
 
-        // ---- absmax: per slot over its 8 lanes (lane bits 0, 1 and 5)
-        float m[SETS];
+        // ---- absmax: per slot over its 8 lanes (lane bits 0, 1 and 5); for INT4 with 128-channel
+        // groups, per half slot: channel bit 7 is the register pair (registers 0, 1 | 2, 3)
+        constexpr int HS = (BITS == 4 && LG == 7) ? 2 : 1;   // scale groups per slot
+        float m[SETS][HS];
 #pragma unroll
         for (int s = 0; s < SETS; ++s) {
-            float a = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int hs = 0; hs < HS; ++hs) {
+                float a = 0.0f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(v[s][r][e]));
-            a = __builtin_fmaxf(a, dpp_xor1(a));
-            a = __builtin_fmaxf(a, dpp_xor2(a));
-            uint32_t lo = __float_as_uint(a), hi = lo;
-            swap32(lo, hi);
-            m[s] = __builtin_fmaxf(__uint_as_float(lo), __uint_as_float(hi));
+                for (int r = hs * (4 / HS); r < (hs + 1) * (4 / HS); ++r)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(v[s][r][e]));
+                a = __builtin_fmaxf(a, dpp_xor1(a));
+                a = __builtin_fmaxf(a, dpp_xor2(a));
+                uint32_t lo = __float_as_uint(a), hi = lo;
+                swap32(lo, hi);
+                m[s][hs] = __builtin_fmaxf(__uint_as_float(lo), __uint_as_float(hi));
+            }
         }
 
         // sign left on this lane's values by the lane-exchange butterflies
         const float lsign = (((LG > 3 ? qd : 0) ^ (LG > 4 ? qd >> 1 : 0)) & 1) ? -1.0f : 1.0f;
-        float mult[SETS];
+        float mult[SETS][HS];
         if constexpr (BITS == 8) {
             // row absmax across slots/waves through LDS (non-negative float bits order like uints).
             // smax[par] was cleared before the previous iteration's first barrier; the other
@@ -218,25 +224,29 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
             if (threadIdx.x < 64) smax[par ^ 1][threadIdx.x] = 0u;
 #pragma unroll
             for (int s = 0; s < SETS; ++s)
-                if (ok[s] && qd == 0 && h == 0) atomicMax(&smax[par][rr[s]], __float_as_uint(m[s]));
+                if (ok[s] && qd == 0 && h == 0) atomicMax(&smax[par][rr[s]], __float_as_uint(m[s][0]));
             __syncthreads();
 #pragma unroll
             for (int s = 0; s < SETS; ++s) {
                 const float amax = __uint_as_float(smax[par][rr[s] < 64 ? rr[s] : 63]);
                 const float sc = (amax * p.cg) / 127.0f;
-                mult[s] = sc > 0.0f ? lsign * (p.cg / sc) : 0.0f;
+                mult[s][0] = sc > 0.0f ? lsign * (p.cg / sc) : 0.0f;
                 if (ok[s] && jj[s] == 0 && qd == 0 && h == 0) static_cast<float *>(p.scale)[row0 + rr[s]] = sc;
             }
         } else {
-            // one fp16 scale per 256-channel group (= slot)
+            // one fp16 scale per g-channel group: the slot (g = 256) or each half of it (g = 128);
+            // a half slot past the end of K (K % 256 == 128) is padding and stores no scale
 #pragma unroll
-            for (int s = 0; s < SETS; ++s) {
-                const __half sh = __float2half_rn((m[s] * p.cg) / 7.0f);
-                const float sc = __half2float(sh);
-                mult[s] = sc > 0.0f ? lsign * (p.cg / sc) : 0.0f;
-                if (ok[s] && qd == 0 && h == 0)
-                    static_cast<__half *>(p.scale)[(int64_t)jj[s] * p.rows + row0 + rr[s]] = sh;
-            }
+            for (int s = 0; s < SETS; ++s)
+#pragma unroll
+                for (int hs = 0; hs < HS; ++hs) {
+                    const __half sh = __float2half_rn((m[s][hs] * p.cg) / 7.0f);
+                    const float sc = __half2float(sh);
+                    mult[s][hs] = sc > 0.0f ? lsign * (p.cg / sc) : 0.0f;
+                    const int64_t grp = (int64_t)jj[s] * HS + hs;
+                    if (ok[s] && qd == 0 && h == 0 && grp * (256 / HS) < K)
+                        static_cast<__half *>(p.scale)[grp * p.rows + row0 + rr[s]] = sh;
+                }
         }
 
         // ---- codes, back to the load layout, store (rows past the group's end lie past
@@ -252,7 +262,7 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
                 for (int r = 0; r < 4; ++r) {
                     uint32_t t[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) t[e] = rne_bits(v[s][r][e], mult[s]);
+                    for (int e = 0; e < 8; ++e) t[e] = rne_bits(v[s][r][e], mult[s][0]);
                     c[r][0] = pack4_i8(t[0], t[1], t[2], t[3]);
                     c[r][1] = pack4_i8(t[4], t[5], t[6], t[7]);
                 }
@@ -269,7 +279,7 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
                 for (int r = 0; r < 4; ++r) {
                     uint32_t t[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) t[e] = rne_bits(v[s][r][e], mult[s]);
+                    for (int e = 0; e < 8; ++e) t[e] = rne_bits(v[s][r][e], mult[s][r / (4 / HS)]);
                     c[r] = pack8_i4(t);
                 }
                 if constexpr (LG > 5) {
@@ -331,12 +341,13 @@ static void rq_launch(int sets, int log2g, dim3 grid, dim3 block, hipStream_t st
     else rq_launch_lg<F32, B, 4>(log2g, grid, block, stream, p);
 }
 
-template <bool F32, int B>
-static void rq_launch_g256(int sets, dim3 grid, dim3 block, hipStream_t stream, const RQParams &p)
+// INT4: the scale group is the rotation group, 256 or 128 channels (checked by the C-ABI layer)
+template <bool F32, int LG>
+static void rq_launch_i4(int sets, dim3 grid, dim3 block, hipStream_t stream, const RQParams &p)
 {
-    if (sets == 1) hipLaunchKernelGGL((rotate_quant_kernel<F32, B, 1, 8>), grid, block, 0, stream, p);
-    else if (sets == 2) hipLaunchKernelGGL((rotate_quant_kernel<F32, B, 2, 8>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((rotate_quant_kernel<F32, B, 4, 8>), grid, block, 0, stream, p);
+    if (sets == 1) hipLaunchKernelGGL((rotate_quant_kernel<F32, 4, 1, LG>), grid, block, 0, stream, p);
+    else if (sets == 2) hipLaunchKernelGGL((rotate_quant_kernel<F32, 4, 2, LG>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((rotate_quant_kernel<F32, 4, 4, LG>), grid, block, 0, stream, p);
 }
 
 hipError_t launch_rotate_quant(const void *x, bool x_f32, int64_t rows, int K, int log2g, int bits, void *q,
@@ -365,13 +376,15 @@ hipError_t launch_rotate_quant(const void *x, bool x_f32, int64_t rows, int K, i
     const int per_cu = RQ_WAVES_PER_CU / W > 1 ? RQ_WAVES_PER_CU / W : 1;
     const int64_t g = (int64_t)cus * per_cu < p.ngroups ? (int64_t)cus * per_cu : p.ngroups;
     const dim3 grid((unsigned)g), block(64 * W);
-    // INT4 always uses group 256 (checked by the C-ABI layer)
+    if (bits == 4 && log2g != 7 && log2g != 8) return hipErrorInvalidValue;
     if (x_f32) {
         if (bits == 8) rq_launch<true, 8>(S, log2g, grid, block, stream, p);
-        else rq_launch_g256<true, 4>(S, grid, block, stream, p);
+        else if (log2g == 8) rq_launch_i4<true, 8>(S, grid, block, stream, p);
+        else rq_launch_i4<true, 7>(S, grid, block, stream, p);
     } else {
         if (bits == 8) rq_launch<false, 8>(S, log2g, grid, block, stream, p);
-        else rq_launch_g256<false, 4>(S, grid, block, stream, p);
+        else if (log2g == 8) rq_launch_i4<false, 8>(S, grid, block, stream, p);
+        else rq_launch_i4<false, 7>(S, grid, block, stream, p);
     }
     return hipGetLastError();
 }

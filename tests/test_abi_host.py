@@ -71,9 +71,10 @@ def test_workspace_bytes(lib):
     for M, N, K in [(4096, 16128, 5376), (17, 256, 512), (12, 8192, 5120), (12, 5120, 25600), (1, 64, 64)]:
         b8 = ws(M, N, K, 8)
         assert b8 % 256 == 0 and b8 >= M * K + 4 * M, (M, N, K)
-    for M, K in [(4096, 5376), (3, 512)]:
+    for M, K in [(4096, 5376), (3, 512), (300, 2688)]:
         b4 = ws(M, 1024, K, 4)
-        assert b4 % 256 == 0 and b4 >= M * K // 2 + 2 * M * (K // 256)
+        # room for 128-channel scale groups too (the query has no group argument)
+        assert b4 % 256 == 0 and b4 >= M * K // 2 + 2 * M * (K // 128)
 
 
 def test_workspace_bytes_w4a8(lib):
@@ -110,9 +111,9 @@ def test_packed_bytes_w4a8(lib):
 def test_packed_bytes_w4a4(lib):
     pb = lib.convrot_packed_bytes_w4a4
     assert pb(-1, 512) == 0 and pb(64, 320) == 0 and pb(64, 0) == 0 and pb(64, 131072 + 256) == 0
-    assert pb(0, 512) == 0
+    assert pb(0, 512) == 0 and pb(64, 192) == 0
     # 32-row blocks x 64-channel K-steps of 1536 bytes (0.75 bytes per code, rows padded to 32)
-    for N, K in [(32, 256), (1, 256), (10752, 5376), (1000, 5120), (8, 131072)]:
+    for N, K in [(32, 256), (1, 256), (10752, 5376), (1000, 5120), (8, 131072), (64, 2688), (40, 128)]:
         assert pb(N, K) == -(-N // 32) * (K // 64) * 1536, (N, K)
 
 
@@ -183,7 +184,7 @@ CASES = [
     ("convrot_quantize_act", q_args(group=3), "CONVROT_ERR_GROUP"),
     ("convrot_quantize_act", q_args(group=512), "CONVROT_ERR_GROUP"),
     ("convrot_quantize_act", q_args(K=192, group=128), "CONVROT_ERR_SHAPE"),
-    ("convrot_quantize_act", q_args(bits=4, group=128), "CONVROT_ERR_GROUP"),
+    ("convrot_quantize_act", q_args(bits=4, group=64), "CONVROT_ERR_GROUP"),
     ("convrot_quantize_act", q_args(bits=4, K=320, group=64), "CONVROT_ERR_GROUP"),
     ("convrot_quantize_act", q_args(x=MIS), "CONVROT_ERR_ALIGN"),
     ("convrot_quantize_act", q_args(q=MIS), "CONVROT_ERR_ALIGN"),
@@ -205,7 +206,9 @@ CASES = [
     ("convrot_linear", lin_args(wsb=16), "CONVROT_ERR_WORKSPACE"),
     ("convrot_linear", lin_args(ws=E + 16), "CONVROT_ERR_WORKSPACE"),
     # W4A4 linear
-    ("convrot_linear_w4a4", w4_args(group=128), "CONVROT_ERR_GROUP"),
+    ("convrot_linear_w4a4", w4_args(group=64), "CONVROT_ERR_GROUP"),
+    ("convrot_linear_w4a4", w4_args(K=384), "CONVROT_ERR_SHAPE"),         # group 256 must divide K
+    ("convrot_linear_w4a4", w4_args(K=128, group=128), "CONVROT_ERR_SHAPE"),   # K >= 256
     ("convrot_linear_w4a4", w4_args(K=320, group=64), "CONVROT_ERR_GROUP"),
     ("convrot_linear_w4a4", w4_args(N=252), "CONVROT_ERR_SHAPE"),
     ("convrot_linear_w4a4", w4_args(sw=None), "CONVROT_ERR_NULL"),
@@ -216,7 +219,7 @@ CASES = [
     # the FP6 tiles live in the workspace even for pre-quantized activations
     ("convrot_linear_w4a4", w4_args(x=None, xq=A, xs=C, ws=None, wsb=0), "CONVROT_ERR_WORKSPACE"),
     # W4A4 with pre-encoded weights, and the one-time re-encode
-    ("convrot_linear_w4a4_packed", w4_args(group=128), "CONVROT_ERR_GROUP"),
+    ("convrot_linear_w4a4_packed", w4_args(group=64), "CONVROT_ERR_GROUP"),
     ("convrot_linear_w4a4_packed", w4_args(N=252), "CONVROT_ERR_SHAPE"),
     ("convrot_linear_w4a4_packed", w4_args(wq=None), "CONVROT_ERR_NULL"),
     ("convrot_linear_w4a4_packed", w4_args(sw=None), "CONVROT_ERR_NULL"),

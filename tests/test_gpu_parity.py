@@ -185,10 +185,17 @@ def test_linear_dynamic_group_adaln_width(cr):
         P.say("dynamic-group linear M=%d N=%d K=%d g=%d" % (M, N, K, g))
         x, w, b = workloads.ragged_case(M, K, N, seed=11)
         _linear_case(cr, x, w, b, g)
-    # the INT4 paths keep their 256-channel scale groups: rejected, not silently regrouped
+    # W4A4 takes the same group (128-channel rotation and scale groups), against the oracle
+    for M, N in [(12, 1000), (300, 2048)]:
+        P.say("dynamic-group W4A4 M=%d N=%d K=%d g=%d" % (M, N, K, g))
+        _w4a4_case(cr, *workloads.ragged_case(M, K, N, seed=12), g)
+    # the W4A8 decode path keeps 256-channel groups: its re-layout rejects the width (256 does
+    # not divide it), nothing is silently regrouped
     w4 = workloads.gaussian_weights(64, K, cfg=94).to(DEV)
-    with pytest.raises(cr.ConvRotError, match="GROUP"):
-        cr.prepare_weight(w4, g, 4)
+    wq4, ws4 = cr.prepare_weight(w4, g, 4)
+    assert ws4.shape == (K // g, 64)
+    with pytest.raises(cr.ConvRotError, match="SHAPE|GROUP"):
+        cr.pack_weight_w4a8(wq4, ws4)
 
 
 def test_linear_prefill_full_size_sampled(cr):
@@ -255,16 +262,18 @@ def test_linear_empty_and_repeat(cr):
 
 # ------------------------------------------------------------------ W4A4
 
-W4_QUANT_CASES = [(4, 512), (37, 768), (300, 5376), (12, 25600)]
+W4_QUANT_CASES = [(4, 512, 256), (37, 768, 256), (300, 5376, 256), (12, 25600, 256), (37, 2688, 128),
+                  (5, 384, 128), (64, 1024, 128)]
 
 
-@pytest.mark.parametrize("rows,K", W4_QUANT_CASES)
-def test_quantize_int4_parity(cr, rows, K):
-    P.say("quantize int4 rows=%d K=%d" % (rows, K))
+@pytest.mark.parametrize("rows,K,g", W4_QUANT_CASES)
+def test_quantize_int4_parity(cr, rows, K, g):
+    P.say("quantize int4 rows=%d K=%d g=%d" % (rows, K, g))
     x, _, _ = workloads.ragged_case(rows, K, 8, seed=rows + K)
-    q, s = cr.quantize_act(x.to(DEV), 256, 4)
+    q, s = cr.quantize_act(x.to(DEV), g, 4)
     torch.cuda.synchronize()
-    c, sr, pr = orc.prepare_i4(_x64(x), 256)
+    assert s.shape == (K // g, rows)
+    c, sr, pr = orc.prepare_i4(_x64(x), g)
     P.check_scales_f16(_np(s).T, sr)
     P.check_codes(orc.unpack_i4(_np(q)), c, "int4 codes", rate=1e-3)
 
@@ -336,45 +345,49 @@ def test_pack_w4a4_layout(cr, N, K):
     assert np.array_equal(_unpack_w4a4_tiles(_np(wp), N, K), cw.astype(np.int64))
 
 
-W4_LINEAR_CASES = [(4, 256, 512), (130, 264, 768), (257, 1024, 5376), (12, 1024, 5120)]
+W4_LINEAR_CASES = [(4, 256, 512, 256), (130, 264, 768, 256), (257, 1024, 5376, 256), (12, 1024, 5120, 256),
+                   (130, 264, 384, 128), (257, 520, 2688, 128)]
 
 
-@pytest.mark.parametrize("M,N,K", W4_LINEAR_CASES)
-def test_linear_w4a4_packed_matches(cr, M, N, K):
+@pytest.mark.parametrize("M,N,K,g", W4_LINEAR_CASES)
+def test_linear_w4a4_packed_matches(cr, M, N, K, g):
     # the pre-encoded weights give the per-call path's result bit for bit, with x and with xq
-    P.say("linear_w4a4_packed M=%d N=%d K=%d" % (M, N, K))
+    P.say("linear_w4a4_packed M=%d N=%d K=%d g=%d" % (M, N, K, g))
     x, w, b = workloads.ragged_case(M, K, N, seed=6)
     xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
-    wq, ws = cr.prepare_weight(wd, 256, 4)
+    wq, ws = cr.prepare_weight(wd, g, 4)
     wp = cr.pack_weight_w4a4(wq)
-    xq, xs = cr.quantize_act(xd, 256, 4)
-    y1 = cr.linear_w4a4(xd, wq, ws, bd)
-    y2 = cr.linear_w4a4_packed(xd, wp, ws, bd)
-    y3 = cr.linear_w4a4_packed(None, wp, ws, bd, xq=xq, x_scale=xs)
-    y4 = cr.linear_w4a4_packed(None, wp, ws, None, xq=xq, x_scale=xs)
+    xq, xs = cr.quantize_act(xd, g, 4)
+    y1 = cr.linear_w4a4(xd, wq, ws, bd, group=g)
+    y2 = cr.linear_w4a4_packed(xd, wp, ws, bd, group=g)
+    y3 = cr.linear_w4a4_packed(None, wp, ws, bd, group=g, xq=xq, x_scale=xs)
+    y4 = cr.linear_w4a4_packed(None, wp, ws, None, group=g, xq=xq, x_scale=xs)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(y1, y3)
-    yown = orc.linear_i4(orc.unpack_i4(_np(xq)), _np(xs).T, orc.unpack_i4(_np(wq)), _np(ws).T, None, 256)
+    yown = orc.linear_i4(orc.unpack_i4(_np(xq)), _np(xs).T, orc.unpack_i4(_np(wq)), _np(ws).T, None, g)
     P.check_y(_x64(y4), yown, "y (no bias, own codes)", strict_frac=1e-4)
 
 
-@pytest.mark.parametrize("M,N,K", W4_LINEAR_CASES)
-def test_linear_w4a4_parity(cr, M, N, K):
-    P.say("linear_w4a4 M=%d N=%d K=%d" % (M, N, K))
-    x, w, b = workloads.ragged_case(M, K, N, seed=5)
+def _w4a4_case(cr, x, w, b, g):
     xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
-    wq, ws = cr.prepare_weight(wd, 256, 4)
-    y = cr.linear_w4a4(xd, wq, ws, bd)
-    xq, xs = cr.quantize_act(xd, 256, 4)
+    wq, ws = cr.prepare_weight(wd, g, 4)
+    y = cr.linear_w4a4(xd, wq, ws, bd, group=g)
+    xq, xs = cr.quantize_act(xd, g, 4)
     torch.cuda.synchronize()
-    ref = orc.linear_w4a4(_x64(x), _x64(w), b.numpy(), 256)
+    ref = orc.linear_w4a4(_x64(x), _x64(w), b.numpy(), g)
     P.check_scales_f16(_np(ws).T, ref["sw"], "sw16")
     P.check_scales_f16(_np(xs).T, ref["sx"], "sx16")
     # y against the oracle evaluated on the GPU's own codes and scales (exact integer part) ...
-    yown = orc.linear_i4(orc.unpack_i4(_np(xq)), _np(xs).T, orc.unpack_i4(_np(wq)), _np(ws).T, b.numpy(), 256)
+    yown = orc.linear_i4(orc.unpack_i4(_np(xq)), _np(xs).T, orc.unpack_i4(_np(wq)), _np(ws).T, b.numpy(), g)
     P.check_y(_x64(y), yown, "y (own codes)", strict_frac=1e-4)
     # ... and against the oracle end to end
     P.check_y(_x64(y), ref["y"], "y (oracle codes)", strict_frac=2e-2)
+
+
+@pytest.mark.parametrize("M,N,K,g", W4_LINEAR_CASES)
+def test_linear_w4a4_parity(cr, M, N, K, g):
+    P.say("linear_w4a4 M=%d N=%d K=%d g=%d" % (M, N, K, g))
+    _w4a4_case(cr, *workloads.ragged_case(M, K, N, seed=5), g)
 
 
 def test_linear_w4a4_full_size_sampled(cr):

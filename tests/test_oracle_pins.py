@@ -261,13 +261,13 @@ def test_int4_quantizer_brute_force_and_bounds(oracle):
             assert np.array_equal(best, c[r, j * g:(j + 1) * g].astype(np.int64))
 
 
-def test_int4_group_sums_and_unit_scales(oracle):
+@pytest.mark.parametrize("g", [256, 128])
+def test_int4_group_sums_and_unit_scales(oracle, g):
     """With all scales 1 the W4A4 output is the plain integer product (exact), and each group
-    partial sum is bounded by g * 7 * 7."""
+    partial sum is bounded by g * 7 * 7; 128 is the dynamic group of widths 256 does not divide."""
     rng = np.random.default_rng(9)
-    g = 256
-    cx = rng.integers(-7, 8, size=(5, 512), dtype=np.int8)
-    cw = rng.integers(-7, 8, size=(9, 512), dtype=np.int8)
+    cx = rng.integers(-7, 8, size=(5, 2 * g), dtype=np.int8)
+    cw = rng.integers(-7, 8, size=(9, 2 * g), dtype=np.int8)
     ones = np.ones((5, 2), np.float16), np.ones((9, 2), np.float16)
     y = oracle.linear_i4(cx, ones[0], cw, ones[1], None, g)
     assert np.array_equal(y, (cx.astype(np.int64) @ cw.astype(np.int64).T).astype(np.float64))
