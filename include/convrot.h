@@ -61,6 +61,10 @@ typedef enum convrot_status {
 enum { CONVROT_DTYPE_F32 = 0, CONVROT_DTYPE_BF16 = 1 };
 
 #define CONVROT_MAX_K 131072
+/* The tiled GEMMs (the W8A8 linear at M > 16 and every W4A4 call) need N < CONVROT_GEMM_MAX_N:
+ * their epilogue addresses a 32-row block of the output with a 32-bit byte offset.  The decode
+ * GEMVs (M <= 16) take any N < 2^31.  A larger N returns CONVROT_ERR_SHAPE. */
+#define CONVROT_GEMM_MAX_N 16777216
 
 /*
  * Offline weight preparation: rotate each weight row by R and quantize it

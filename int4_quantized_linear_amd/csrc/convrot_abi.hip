@@ -49,6 +49,15 @@ int check_shape(int64_t M, int64_t N, int64_t K, int group, const char *who)
     return CONVROT_OK;
 }
 
+// N limit of the tiled GEMMs (their 32-row output blocks use 32-bit byte offsets).
+int check_gemm_n(int64_t N, const char *who)
+{
+    if (N >= CONVROT_GEMM_MAX_N)
+        return fail(CONVROT_ERR_SHAPE, "%s: N=%lld; the tiled GEMM (M > 16, or W4A4) needs N < %d", who, (long long)N,
+                    CONVROT_GEMM_MAX_N);
+    return CONVROT_OK;
+}
+
 // One cached answer per device: is it gfx950?
 int check_device()
 {
@@ -193,6 +202,7 @@ int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_
     const char *who = "convrot_linear";
     int rc = check_shape(M, N, K, group, who);
     if (rc) return rc;
+    if (M > 16 && (rc = check_gemm_n(N, who))) return rc;
     if (M == 0 || N == 0) return CONVROT_OK;
     if (!wq || !w_scale || !y) return fail(CONVROT_ERR_NULL, "%s: wq, w_scale and y must be non-NULL", who);
     if (!x && (!xq || !x_scale)) return fail(CONVROT_ERR_NULL, "%s: give x, or both xq and x_scale", who);
@@ -232,6 +242,7 @@ int convrot_gemm_i8_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N
     const char *who = "convrot_gemm_i8_i32";
     int rc = check_shape(M, N, K, 1, who);
     if (rc) return rc;
+    if (M > 16 && (rc = check_gemm_n(N, who))) return rc;
     if (M == 0 || N == 0) return CONVROT_OK;
     if (!xq || !wq || !acc) return fail(CONVROT_ERR_NULL, "%s: xq, wq and acc must be non-NULL", who);
     if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(acc, 16)) return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
@@ -260,6 +271,7 @@ int linear_w4a4(const char *who, const void *x, int x_dtype, const uint8_t *xq, 
 {
     int rc = check_shape(M, N, K, group, who);
     if (rc) return rc;
+    if ((rc = check_gemm_n(N, who))) return rc;
     if ((group != 256 && group != 128) || K % group)
         return fail(CONVROT_ERR_GROUP, "%s: W4A4 needs group 256 or 128 dividing K (group=%d, K=%lld)", who, group,
                     (long long)K);
@@ -407,6 +419,7 @@ int convrot_gemm_i4_i32(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t
     const char *who = "convrot_gemm_i4_i32";
     int rc = check_shape(M, N, K, 256, who);
     if (rc) return rc;
+    if ((rc = check_gemm_n(N, who))) return rc;
     if (K % 256 || N % 8) return fail(CONVROT_ERR_SHAPE, "%s: needs K %% 256 == 0 and N %% 8 == 0", who);
     if (M == 0 || N == 0) return CONVROT_OK;
     if (!xq || !wq || !acc) return fail(CONVROT_ERR_NULL, "%s: xq, wq and acc must be non-NULL", who);

@@ -373,6 +373,8 @@ hipError_t launch_gemm_i8(const int8_t *xq, const int8_t *wq, const float *sx, c
                           void *y, Epi epi, int64_t M, int64_t N, int K, hipStream_t stream)
 {
     if (M <= 0 || N <= 0) return hipSuccess;
+    // the epilogue's byte offset within a 32-row output block, 32 * N * 4 bytes at most, is 32-bit
+    if (N >= ((int64_t)1 << 24)) return hipErrorInvalidValue;
     static int cus = [] {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)

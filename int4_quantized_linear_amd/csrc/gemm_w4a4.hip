@@ -537,6 +537,8 @@ hipError_t launch_gemm_w4a4(const uint8_t *xq, const uint8_t *wq, bool w_tiled, 
                             int group, void *ws, hipStream_t stream)
 {
     if (M <= 0 || N <= 0) return hipSuccess;
+    // the epilogue's byte offset within a 32-row output block, 32 * N * 4 bytes at most, is 32-bit
+    if (N >= ((int64_t)1 << 24)) return hipErrorInvalidValue;
     // scale groups of 2 K-tiles (256 channels) or 1 (128); at least 2 K-tiles (bias ring)
     const int gkt = group / BK;
     if ((gkt != 1 && gkt != 2) || K % group || K < 2 * BK) return hipErrorInvalidValue;

@@ -205,12 +205,16 @@ CASES = [
     ("convrot_linear", lin_args(ws=None), "CONVROT_ERR_WORKSPACE"),
     ("convrot_linear", lin_args(wsb=16), "CONVROT_ERR_WORKSPACE"),
     ("convrot_linear", lin_args(ws=E + 16), "CONVROT_ERR_WORKSPACE"),
+    # the tiled GEMM's N limit (2^24); the decode GEMV (M <= 16) takes a larger N
+    ("convrot_linear", lin_args(N=1 << 24), "CONVROT_ERR_SHAPE"),
+    ("convrot_linear", lin_args(M=16, N=1 << 24, wq=None), "CONVROT_ERR_NULL"),
     # W4A4 linear
     ("convrot_linear_w4a4", w4_args(group=64), "CONVROT_ERR_GROUP"),
     ("convrot_linear_w4a4", w4_args(K=384), "CONVROT_ERR_SHAPE"),         # group 256 must divide K
     ("convrot_linear_w4a4", w4_args(K=128, group=128), "CONVROT_ERR_SHAPE"),   # K >= 256
     ("convrot_linear_w4a4", w4_args(K=320, group=64), "CONVROT_ERR_GROUP"),
     ("convrot_linear_w4a4", w4_args(N=252), "CONVROT_ERR_SHAPE"),
+    ("convrot_linear_w4a4", w4_args(M=1, N=1 << 24), "CONVROT_ERR_SHAPE"),
     ("convrot_linear_w4a4", w4_args(sw=None), "CONVROT_ERR_NULL"),
     ("convrot_linear_w4a4", w4_args(x=None, xs=C), "CONVROT_ERR_NULL"),
     ("convrot_linear_w4a4", w4_args(dt=9), "CONVROT_ERR_DTYPE"),
@@ -221,6 +225,7 @@ CASES = [
     # W4A4 with pre-encoded weights, and the one-time re-encode
     ("convrot_linear_w4a4_packed", w4_args(group=64), "CONVROT_ERR_GROUP"),
     ("convrot_linear_w4a4_packed", w4_args(N=252), "CONVROT_ERR_SHAPE"),
+    ("convrot_linear_w4a4_packed", w4_args(N=1 << 24), "CONVROT_ERR_SHAPE"),
     ("convrot_linear_w4a4_packed", w4_args(wq=None), "CONVROT_ERR_NULL"),
     ("convrot_linear_w4a4_packed", w4_args(sw=None), "CONVROT_ERR_NULL"),
     ("convrot_linear_w4a4_packed", w4_args(wq=B + 8), "CONVROT_ERR_ALIGN"),
@@ -256,10 +261,13 @@ CASES = [
     ("convrot_pack_weight_w4a8", (A, C, 64, 512, B + 8, None), "CONVROT_ERR_ALIGN"),
     # integer cores
     ("convrot_gemm_i8_i32", (A, B, 32, 256, 96, C, None, 0, None), "CONVROT_ERR_SHAPE"),
+    ("convrot_gemm_i8_i32", (A, B, 32, 1 << 24, 512, C, None, 0, None), "CONVROT_ERR_SHAPE"),
+    ("convrot_gemm_i8_i32", (None, B, 16, 1 << 24, 512, C, None, 0, None), "CONVROT_ERR_NULL"),
     ("convrot_gemm_i8_i32", (None, B, 32, 256, 512, C, None, 0, None), "CONVROT_ERR_NULL"),
     ("convrot_gemm_i8_i32", (A, B, 32, 256, 512, MIS, None, 0, None), "CONVROT_ERR_ALIGN"),
     ("convrot_gemm_i4_i32", (A, B, 32, 256, 320, C, E, 1 << 30, None), "CONVROT_ERR_SHAPE"),
     ("convrot_gemm_i4_i32", (A, B, 32, 250, 512, C, E, 1 << 30, None), "CONVROT_ERR_SHAPE"),
+    ("convrot_gemm_i4_i32", (A, B, 32, 1 << 24, 512, C, E, 1 << 30, None), "CONVROT_ERR_SHAPE"),
     ("convrot_gemm_i4_i32", (A, None, 32, 256, 512, C, E, 1 << 30, None), "CONVROT_ERR_NULL"),
     ("convrot_gemm_i4_i32", (A, B + 4, 32, 256, 512, C, E, 1 << 30, None), "CONVROT_ERR_ALIGN"),
     ("convrot_gemm_i4_i32", (A, B, 32, 256, 512, C, None, 0, None), "CONVROT_ERR_WORKSPACE"),
