@@ -52,8 +52,8 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a4", "stack", "copy"], default="all",
                     help="restrict the measured workloads (profiling runs); 'copy' = the counter calibration copy")
@@ -91,8 +91,27 @@ def traffic_from_profiles(key: str, current_hash: str):
 # timing helpers
 
 
+SETTLE_S = 0.3
+
+
+def settle(fn, torch, seconds: float = SETTLE_S):
+    """Repeat fn(i) untimed for `seconds` of wall time.  The host-side input generation before
+    each section leaves the GPU idle for seconds, and its clocks need a few hundred milliseconds
+    of load to reach their steady state (measured on the prefill step: 371 us per GEMM after
+    5 warm-up steps, 317 us once settled)."""
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def timed_loop(fn, steps: int, warmup: int, torch):
-    """Run fn(i) warmup + steps times; returns (wall ms per step, [per-call event lists])."""
+    """Settle, run fn(i) warmup times, then time exactly `steps` calls; returns (wall ms per
+    step, [per-call event lists])."""
+    settle(fn, torch)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -120,7 +139,7 @@ def graph_time_us(torch, launch, n_calls: int, reps: int) -> float:
     torch.cuda.synchronize()
     per = []
     with torch.cuda.stream(s):
-        g.replay()                          # warm replay
+        settle(lambda i: g.replay(), torch)
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(s)
@@ -370,6 +389,7 @@ def bench_stack(cr, wl, torch, layers: int):
 
     def timed(fuse):
         per_pass = []
+        settle(lambda i: layer(i % layers, fuse), torch)
         for rep in range(3):                      # pass 0 warms up
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(layers + 1)]
             ev[0].record(st)
