@@ -228,6 +228,57 @@ def test_linear_prefill_full_size_sampled(cr):
     assert np.array_equal(accg[mr[ii], nr[jj]], orc.gemm_i32_pairs(_np(xq), _np(wq), mr[ii], nr[jj]))
 
 
+def _stack_groups():
+    """The layer stack's linears grouped by shared input, as the bench fuses them."""
+    groups = []
+    for i, (name, K, N) in enumerate(workloads.STACK_MATRICES):
+        inp = workloads.STACK_INPUT_OF[name]
+        if groups and groups[-1][0] == inp:
+            groups[-1][2].append((i, N))
+        else:
+            groups.append((inp, K, [(i, N)]))
+    return groups
+
+
+@pytest.mark.parametrize("inp,K,members", _stack_groups(), ids=[g[0] for g in _stack_groups()])
+def test_linear_stack_shapes_full_size_sampled(cr, inp, K, members):
+    """The layer stack's GEMMs at their full size (M = 2048; q|k|v and gate|up as one GEMM over the
+    concatenated weight rows, o with K = 8192, down with K = 25600), on layer 0's device-drawn
+    inputs; the oracle on 256 sampled token rows / weight rows and 4096 sampled outputs."""
+    M = workloads.STACK_M
+    j = [name for name, _ in workloads.STACK_INPUTS].index(inp)
+    P.say("stack %s: M=%d K=%d N=%d" % (inp, M, K, sum(N for _, N in members)))
+    x = workloads.stack_acts(0, j, M, K, DEV)
+    w = torch.cat([workloads.stack_weight(0, i, N, K, DEV) for i, N in members])
+    N = w.shape[0]
+    wq, ws = cr.prepare_weight(w, 256, 8)
+    y = cr.linear(x, wq, ws, group=256)
+    xq, xs = cr.quantize_act(x, 256, 8)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(K + N)
+    mr = np.sort(rng.choice(M, 256, replace=False))
+    nr = np.sort(rng.choice(N, 256, replace=False))
+    x_h, w_h = x[torch.from_numpy(mr).to(DEV)].cpu(), w[torch.from_numpy(nr).to(DEV)].cpu()
+    qx, sx = orc.quantize_act_i8(_x64(x_h), 256)
+    qw, sw = orc.prepare_weight_i8(_x64(w_h), 256)
+    P.check_codes(_np(xq)[mr], qx, "qx rows")
+    P.check_scales_f32(_np(xs)[mr], sx, "sx rows")
+    P.check_codes(_np(wq)[nr], qw, "qw rows")
+    P.check_scales_f32(_np(ws)[nr], sw, "sw rows")
+    ii = rng.integers(0, 256, 4096)
+    jj = rng.integers(0, 256, 4096)
+    acc = orc.gemm_i32_pairs(qx, qw, ii, jj)
+    yref = acc.astype(np.float64) * sx[ii].astype(np.float64) * sw[jj].astype(np.float64)
+    P.check_y(_x64(y)[mr[ii], nr[jj]], yref, "sampled y")
+    # the integer core on the GPU's own codes, bit-exact on the same pairs
+    accg = cr.gemm_i8_i32(xq, wq)
+    torch.cuda.synchronize()
+    ti, tj = torch.from_numpy(mr[ii]).to(DEV), torch.from_numpy(nr[jj]).to(DEV)
+    got = accg[ti, tj].cpu().numpy()
+    del accg
+    assert np.array_equal(got, orc.gemm_i32_pairs(_np(xq), _np(wq), mr[ii], nr[jj]))
+
+
 def test_linear_concatenated_rows_equal_separate(cr):
     # Linears sharing an input can run as one GEMM over their concatenated weight rows: row-wise
     # scales make the concatenation's preparation the concatenation of the separate ones, and
