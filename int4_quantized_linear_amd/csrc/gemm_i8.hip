@@ -391,6 +391,8 @@ hipError_t launch_gemm_i8(const int8_t *xq, const int8_t *wq, const float *sx, c
     p.M = M;
     p.N = N;
     p.K = K;
+    // the tile walk counts tiles in int
+    if (((M + BM - 1) / BM) * ((N + BN - 1) / BN) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     p.tiles_m = (int)((M + BM - 1) / BM);
     p.tiles_n = (int)((N + BN - 1) / BN);
     const int T = p.tiles_m * p.tiles_n;

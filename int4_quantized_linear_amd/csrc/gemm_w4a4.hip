@@ -539,6 +539,8 @@ hipError_t launch_gemm_w4a4(const uint8_t *xq, const uint8_t *wq, bool w_tiled, 
     if (M <= 0 || N <= 0) return hipSuccess;
     // the epilogue's byte offset within a 32-row output block, 32 * N * 4 bytes at most, is 32-bit
     if (N >= ((int64_t)1 << 24)) return hipErrorInvalidValue;
+    // the tile walk counts tiles in int
+    if (((M + BM - 1) / BM) * ((N + BN - 1) / BN) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     // scale groups of 2 K-tiles (256 channels) or 1 (128); at least 2 K-tiles (bias ring)
     const int gkt = group / BK;
     if ((gkt != 1 && gkt != 2) || K % group || K < 2 * BK) return hipErrorInvalidValue;
