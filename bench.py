@@ -368,6 +368,11 @@ def bench_stack(cr, wl, torch, layers: int):
     xs = {inp: torch.empty((M,), dtype=torch.float32, device=dev) for inp, _ in wl.STACK_INPUTS}
     ys = {inp: torch.empty((M, sum(N for _, _, N in members)), dtype=torch.bfloat16, device=dev)
           for inp, members in groups}
+    # one workspace for every GEMM of the layer (stream order serialises them): room for the
+    # split-K tail of the GEMMs whose tiles leave the grid's last round partly idle
+    shapes = [(K, N) for _, K, N in wl.STACK_MATRICES] + [(f[1], f[2]) for f in W[0]]
+    wsz = max(cr.workspace_bytes(M, N, K, 8) for K, N in shapes)
+    wsb = torch.empty(max(wsz, 256), dtype=torch.uint8, device=dev)
 
     def layer(L, fuse):
         for inp, K in wl.STACK_INPUTS:
@@ -377,14 +382,14 @@ def bench_stack(cr, wl, torch, layers: int):
             y = ys[inp]
             if fuse:
                 cr._call("convrot_linear", None, 0, xq[inp].data_ptr(), xs[inp].data_ptr(), M, NT, K, 256,
-                         wq.data_ptr(), sw.data_ptr(), None, y.data_ptr(), None, 0, st.cuda_stream)
+                         wq.data_ptr(), sw.data_ptr(), None, y.data_ptr(), wsb.data_ptr(), wsz, st.cuda_stream)
                 continue
             n0 = 0
             for _, name, N in members:
                 # the separate linear writes its own [M, N] output (a contiguous block of y)
                 cr._call("convrot_linear", None, 0, xq[inp].data_ptr(), xs[inp].data_ptr(), M, N, K, 256,
                          wq[n0:n0 + N].data_ptr(), sw[n0:n0 + N].data_ptr(), None, y.view(-1)[M * n0:].data_ptr(),
-                         None, 0, st.cuda_stream)
+                         wsb.data_ptr(), wsz, st.cuda_stream)
                 n0 += N
 
     def timed(fuse):

@@ -93,9 +93,11 @@ int convrot_quantize_act(const void *x, int x_dtype, int64_t M, int64_t K, int g
  * Workspace bytes needed by convrot_linear (bits 8) / convrot_linear_w4a4 (bits 4) for this
  * shape; 0 on invalid arguments.  The workspace must be 256-byte aligned.  It is scratch: the
  * library initialises what it needs on the stream, so any contents are fine on entry and it holds
- * nothing useful afterwards.  The bits-8 workspace holds the quantized activations, so
- * convrot_linear needs it only when it quantizes x itself; convrot_gemm_i8_i32 needs none (it
- * accepts and ignores one); convrot_gemm_i4_i32 needs the bits-4 size.  Besides the activation
+ * nothing useful afterwards.  The bits-8 workspace holds the quantized activations (M*K bytes,
+ * then 4*M, each rounded up to 256), so convrot_linear needs that much only when it quantizes x
+ * itself.  For M > 16 and N % 8 == 0 it may add room for the GEMM's split-K tail (below), so
+ * passing the full size is never slower.  convrot_gemm_i8_i32 needs none (it accepts and ignores
+ * one); convrot_gemm_i4_i32 needs the bits-4 size.  Besides the activation
  * codes and scales, the bits-4 workspace holds both operands re-encoded as FP6 in matrix-core
  * order (1536 bytes per 32 rows x 64 channels, (ceil(M/32) + ceil(N/32)) * K/64 pieces).
  */
@@ -109,6 +111,14 @@ size_t convrot_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits);
  *   wq, w_scale from convrot_prepare_weight(bits = 8); bias fp32 [N] or NULL; y bf16 [M, N].
  * M <= 16 runs the weight-streaming GEMV, larger M the MFMA GEMM.  With x = NULL the workspace
  * may be NULL.
+ * Split-K tail: the GEMM walks 256 x 256 output tiles with one persistent workgroup per CU.  When
+ * the tiles leave its last round badly under-filled (few tiles: mid-size M, small N), the tail
+ * tiles are computed as K-slices, their exact int32 partial sums are stored in the workspace past
+ * the quantized activations, and a second kernel sums them and applies the same epilogue, so the
+ * outputs are bit-identical either way.  This needs workspace_bytes >= convrot_workspace_bytes(M,
+ * N, K, 8) (with x = NULL too); a smaller or NULL workspace runs without it.  The two kernels run
+ * in stream order, so calls on one stream may share a workspace; calls that overlap on different
+ * streams need their own.
  */
 int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_scale, int64_t M, int64_t N,
                    int64_t K, int group, const int8_t *wq, const float *w_scale, const float *bias, void *y,

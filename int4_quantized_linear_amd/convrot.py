@@ -146,17 +146,23 @@ def quantize_act(x: torch.Tensor, group: int = 256, bits: int = 8):
 
 def linear(x: torch.Tensor | None, wq: torch.Tensor, w_scale: torch.Tensor, bias: torch.Tensor | None = None,
            group: int = 256, xq: torch.Tensor | None = None, x_scale: torch.Tensor | None = None,
-           out: torch.Tensor | None = None) -> torch.Tensor:
+           out: torch.Tensor | None = None, split_k: bool = True) -> torch.Tensor:
     """INT8 ConvRot linear: y = bf16((q(xR) . q(wR)^T) * sx * sw + bias).  Pass x (bf16/fp32 [M,K])
-    or a pre-quantized (xq, x_scale) pair."""
+    or a pre-quantized (xq, x_scale) pair.  The workspace passed has room for the GEMM's split-K
+    tail; split_k=False (pre-quantized x only) passes none, so the GEMM runs without it."""
     _check_dev(x, wq, w_scale, bias, xq, x_scale, out)
     N, K = wq.shape
     M = x.shape[0] if x is not None else xq.shape[0]
     dev = wq.device
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    ws = _workspace(M, N, K, 8, dev)
+    if split_k:
+        ws = _workspace(M, N, K, 8, dev)
+    elif x is None:
+        ws = None
+    else:
+        raise ValueError("split_k=False needs a pre-quantized (xq, x_scale) pair")
     _call("convrot_linear", _ptr(x), _dtype_code(x) if x is not None else 0, _ptr(xq), _ptr(x_scale), M, N, K, group,
-          _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y), _ptr(ws), ws.numel(), _stream(dev))
+          _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y), _ptr(ws), ws.numel() if ws is not None else 0, _stream(dev))
     return y
 
 

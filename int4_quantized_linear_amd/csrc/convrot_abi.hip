@@ -88,7 +88,7 @@ int hip_status(hipError_t e, const char *what)
 //   bits 4: [xq packed M*K/2][x_scale fp16 (K/128)*M, enough for either INT4 group][FP6 tiles of
 //           both operands]
 struct WsLayout {
-    size_t xq = 0, xs = 0, tiles = 0, total = 0;
+    size_t xq = 0, xs = 0, tiles = 0, part = 0, total = 0;
 };
 
 WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int bits)
@@ -100,6 +100,9 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int bits)
         off += round256((size_t)(M * K));
         L.xs = off;
         off += round256((size_t)M * 4);
+        // optional: the split-K tail's int32 partial sums (GEMM path only)
+        L.part = off;
+        if (M > 16) off += round256(convrot::gemm_i8_split_bytes(M, N, (int)K));
     } else {
         L.xq = off;
         off += round256((size_t)(M * K / 2));
@@ -212,13 +215,20 @@ int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_
         !aligned(w_scale, 4) || !aligned(y, 16) || (bias && !aligned(bias, 4)))
         return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
     const WsLayout L = ws_layout(M, N, K, 8);
-    if (x && (!workspace || workspace_bytes < L.total || !aligned(workspace, 256)))
-        return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes (got %zu)", who, L.total,
-                    workspace ? workspace_bytes : (size_t)0);
+    if (x && (!workspace || workspace_bytes < L.part || !aligned(workspace, 256)))
+        return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of at least %zu bytes (got %zu)",
+                    who, L.part, workspace ? workspace_bytes : (size_t)0);
     if (M == 0 || N == 0) return CONVROT_OK;
     if ((rc = check_device())) return rc;
 
     uint8_t *ws = static_cast<uint8_t *>(workspace);
+    // room past the quantized x lets an under-filled GEMM split its tail tiles in K
+    void *part = nullptr;
+    size_t part_bytes = 0;
+    if (M > 16 && ws && aligned(ws, 256) && L.total > L.part && workspace_bytes >= L.total) {
+        part = ws + L.part;
+        part_bytes = workspace_bytes - L.part;
+    }
     if (x) {
         int8_t *qx = reinterpret_cast<int8_t *>(ws + L.xq);
         float *sx = reinterpret_cast<float *>(ws + L.xs);
@@ -232,7 +242,7 @@ int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_
     hipError_t e = M <= 16 ? convrot::launch_gemv_i8(xq, wq, x_scale, w_scale, bias, y, convrot::Epi::Bf16, M, N,
                                                       (int)K, stream)
                            : convrot::launch_gemm_i8(xq, wq, x_scale, w_scale, bias, y, convrot::Epi::Bf16, M, N,
-                                                      (int)K, stream);
+                                                      (int)K, part, part_bytes, stream);
     return hip_status(e, M <= 16 ? "gemv_i8" : "gemm_i8");
 }
 
@@ -255,7 +265,8 @@ int convrot_gemm_i8_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N
                           "gemv_i8");
     }
     return hip_status(
-        convrot::launch_gemm_i8(xq, wq, nullptr, nullptr, nullptr, acc, convrot::Epi::Int32, M, N, (int)K, stream),
+        convrot::launch_gemm_i8(xq, wq, nullptr, nullptr, nullptr, acc, convrot::Epi::Int32, M, N, (int)K, nullptr, 0,
+                                stream),
         "gemm_i8");
 }
 

@@ -16,8 +16,15 @@ hipError_t launch_rotate_quant(const void *x, bool x_f32, int64_t rows, int K, i
 enum class Epi { Bf16 = 0, Int32 = 1 };
 
 // y[M,N] = bf16(acc * sx[m] * sw[n] + bias[n])  or  acc32[M,N] = acc,   acc = xq . wq^T  (M > 16).
+// part: optional scratch for the split-K tail (bf16 output only): when the tiles leave the last
+// round of the persistent grid partly idle and part_bytes >= gemm_i8_split_bytes(M, N, K), the
+// tail tiles are computed as K-slices whose int32 partial sums meet in `part`, then a second
+// kernel sums them and applies the epilogue (bit-identical outputs).  part == nullptr: no split.
 hipError_t launch_gemm_i8(const int8_t *xq, const int8_t *wq, const float *sx, const float *sw, const float *bias,
-                          void *y, Epi epi, int64_t M, int64_t N, int K, hipStream_t stream);
+                          void *y, Epi epi, int64_t M, int64_t N, int K, void *part, size_t part_bytes,
+                          hipStream_t stream);
+// Bytes of `part` the split-K tail uses for this shape on the current device (0: no split).
+size_t gemm_i8_split_bytes(int64_t M, int64_t N, int K);
 
 // Same contraction for M <= 16 (weight streaming; K split among the wavefronts of a workgroup,
 // no scratch memory).

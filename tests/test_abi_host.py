@@ -77,6 +77,28 @@ def test_workspace_bytes(lib):
         assert b4 % 256 == 0 and b4 >= M * K // 2 + 2 * M * (K // 128)
 
 
+def _r256(n):
+    return (n + 255) // 256 * 256
+
+
+def test_workspace_bytes_split_k_tail(lib):
+    # On a host without a GPU the grid capacity falls back to MI355X's 256 CUs.
+    ws = lib.convrot_workspace_bytes
+    base = lambda M, K: _r256(M * K) + _r256(4 * M)
+    # under-filled grids whose tail tiles are split: room for the int32 partial slots (256 KiB
+    # each, tail tiles x slices), past the quantized x
+    for M, N, K in [(64, 8192, 5120), (17, 520, 1024), (300, 1000, 4096), (2048, 1024, 5120), (200, 5120, 25600)]:
+        extra = ws(M, N, K, 8) - base(M, K)
+        assert extra > 0 and extra % (256 * 256 * 4) == 0, (M, N, K, extra)
+    # no split: whole rounds but the last nearly full (the prefill shape), a tail that keeps ~3/4
+    # of the CUs busy (160 tiles; the kernel is power-bound there), a short tail after a whole
+    # round (q|k|v: the partial sums' round trip costs what the tail saves), N % 8 != 0 (the
+    # element-store epilogue has no partial-sum path), and the decode GEMV (M <= 16)
+    for M, N, K in [(4096, 16128, 5376), (2048, 5120, 25600), (2048, 5120, 8192), (2048, 10240, 5120),
+                    (130, 1001, 2048), (12, 8192, 5120)]:
+        assert ws(M, N, K, 8) == base(M, K), (M, N, K)
+
+
 def test_workspace_bytes_w4a8(lib):
     ws = lib.convrot_workspace_bytes_w4a8
     assert ws(17, 256, 512) == 0 and ws(-1, 256, 512) == 0 and ws(4, -1, 512) == 0

@@ -279,6 +279,43 @@ def test_linear_stack_shapes_full_size_sampled(cr, inp, K, members):
     assert np.array_equal(got, orc.gemm_i32_pairs(_np(xq), _np(wq), mr[ii], nr[jj]))
 
 
+# Shapes whose tiles leave the last round of the persistent GEMM partly idle, so the tail tiles
+# are split in K (int32 partial sums in the workspace, then a second kernel): mid-size M, ragged
+# M, long K, and the layer stack's k/v projection (N = 1024 at M = 2048: 32 tiles).
+SPLIT_CASES = [(64, 8192, 5120, True), (17, 520, 1024, False), (300, 1000, 4096, True), (130, 1000, 2048, True),
+               (513, 1000, 5376, False), (200, 5120, 25600, True), (2048, 1024, 5120, True)]
+
+
+@pytest.mark.parametrize("M,N,K,with_bias", SPLIT_CASES)
+def test_linear_split_k_tail_bit_identical(cr, M, N, K, with_bias):
+    P.say("split-K tail M=%d N=%d K=%d" % (M, N, K))
+    # the workspace the binding passes has a split region for these shapes
+    assert cr.workspace_bytes(M, N, K, 8) > _r256(M * K) + _r256(4 * M)
+    x = workloads.heavy_tailed_acts(M, K, cfg=95, layer=M).to(DEV)
+    w = workloads.gaussian_weights(N, K, cfg=95, layer=N).to(DEV)
+    b = torch.randn(N, generator=torch.Generator().manual_seed(N)).to(DEV) if with_bias else None
+    xq, xs = cr.quantize_act(x, 256, 8)
+    wq, ws = cr.prepare_weight(w, 256, 8)
+    y_split = cr.linear(None, wq, ws, b, xq=xq, x_scale=xs)
+    y_whole = cr.linear(None, wq, ws, b, xq=xq, x_scale=xs, split_k=False)
+    y_again = cr.linear(x, wq, ws, b)
+    torch.cuda.synchronize()
+    assert torch.equal(y_split, y_whole)
+    assert torch.equal(y_again, y_whole)
+    # and against the oracle on the GPU's own codes
+    rng = np.random.default_rng(M + N + K)
+    ii, jj = rng.integers(0, M, 2048), rng.integers(0, N, 2048)
+    acc = orc.gemm_i32_pairs(_np(xq), _np(wq), ii, jj)
+    yref = acc.astype(np.float64) * _np(xs)[ii].astype(np.float64) * _np(ws)[jj].astype(np.float64)
+    if b is not None:
+        yref += b.cpu().numpy().astype(np.float64)[jj]
+    P.check_y(_x64(y_split)[ii, jj], yref, "sampled y")
+
+
+def _r256(n):
+    return (n + 255) // 256 * 256
+
+
 def test_linear_concatenated_rows_equal_separate(cr):
     # Linears sharing an input can run as one GEMM over their concatenated weight rows: row-wise
     # scales make the concatenation's preparation the concatenation of the separate ones, and
