@@ -676,3 +676,24 @@ def test_decode_linears_run_on_the_callers_stream_and_replay(cr):
     torch.cuda.synchronize()
     _replay_matches(lambda: cr.linear(None, wq8, ws8, xq=xq, x_scale=xs, out=y8), y8, ref8)
     _replay_matches(lambda: cr.linear_w4a8(None, wp, N, xq=xq, x_scale=xs, out=y4), y4, ref4)
+
+
+def test_split_k_gemm_runs_on_the_callers_stream_and_replays(cr):
+    """The split-K tail's two kernels (K-slices writing partial sums, then their reduction) both go
+    to the caller's stream, so a captured graph holds them, and every replay rewrites the partial
+    slots it reads (no state carried between calls)."""
+    M, N, K = 64, 8192, 5120
+    assert cr.workspace_bytes(M, N, K, 8) > _r256(M * K) + _r256(4 * M)     # a split is planned
+    w = workloads.gaussian_weights(N, K, cfg=94).to(DEV)
+    x = workloads.heavy_tailed_acts(M, K, cfg=94, layer=0).to(DEV)
+    b = torch.randn(N, generator=torch.Generator().manual_seed(94)).to(DEV)
+    xq, xs = cr.quantize_act(x, 256, 8)
+    wq, ws = cr.prepare_weight(w, 256, 8)
+    ref = cr.linear(None, wq, ws, b, xq=xq, x_scale=xs).clone()
+    whole = cr.linear(None, wq, ws, b, xq=xq, x_scale=xs, split_k=False)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, whole)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    _replay_matches(lambda: cr.linear(None, wq, ws, b, xq=xq, x_scale=xs, out=y), y, ref)
+    # rotate+quantize, the K-slices and the reduction in one graph
+    _replay_matches(lambda: cr.linear(x, wq, ws, b, out=y), y, ref)
