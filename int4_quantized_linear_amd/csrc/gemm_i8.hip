@@ -14,7 +14,7 @@
 //    along M so that the tiles running at the same time share their weight tile in that XCD's
 //    L2.  8 wavefronts (2 per SIMD, so one covers the other's waits) in 2(N) x 4(M) each own a
 //    128x64 sub-tile as 4x2 blocks of v_mfma_i32_32x32x32_i8 (128 int32 accumulators per lane,
-//    in AGPRs, leaving room for a spill-free epilogue);
+//    about 230 of the 256 registers a wave has at 2 waves per SIMD, with no spills);
 //  * K is streamed 128 bytes per K-tile through 2 LDS stages with buffer_load ... lds (global
 //    -> LDS, no VGPRs).  A row's K-tile is one whole 128-byte cache line and one load
 //    instruction moves 8 such lines, so every line is requested from L2 once (64-byte K-tiles
@@ -33,7 +33,11 @@
 //  * the epilogue converts in registers and stores 16 bytes per lane straight to global memory
 //    (lane pairs exchange halves with v_permlane32_swap so each store covers 8 columns); the
 //    tile's sx/sw/bias are loaded into LDS with its first K-tile (4 rotating buffers: with short
-//    K the load side can run up to 3 tiles ahead).
+//    K the load side can run up to 3 tiles ahead);
+//  * split-K tail: when the tiles leave the grid's last round badly under-filled, the tail tiles
+//    run as K-slices (the walk is over units: whole tiles, then slices), each slice storing its
+//    exact int32 sums to a workspace slot, and split_reduce_kernel sums the slots and applies
+//    the same epilogue arithmetic, so the outputs are bit-identical to the whole-tile path.
 #include <type_traits>
 
 #include "device_common.hpp"
