@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a4", "stack", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a4", "stack", "split", "copy"], default="all",
                     help="restrict the measured workloads (profiling runs); 'copy' = the counter calibration copy")
     ap.add_argument("--stack-layers", type=int, default=64)
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -420,6 +420,53 @@ def bench_stack(cr, wl, torch, layers: int):
     return res
 
 
+SPLIT_SHAPES = [(64, 8192, 5120), (128, 8192, 5120), (32, 25600, 5120), (2048, 1024, 5120)]
+
+
+def bench_split(cr, torch, steps, warmup):
+    """GEMMs whose 256 x 256 tiles leave the persistent grid badly under-filled (mid-size M, the
+    layer stack's k/v projection): the pre-quantized INT8 linear without a workspace (whole tiles
+    only) and with one (the tail tiles split in K, a second kernel summing the int32 partials).
+    Random codes and scales; outputs must be bit-identical."""
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    out = {}
+    for M, N, K in SPLIT_SHAPES:
+        xq = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=g)
+        wq = torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev, generator=g)
+        sx = torch.rand(M, device=dev, generator=g) * 0.01
+        sw = torch.rand(N, device=dev, generator=g) * 0.01
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        wsz = cr.workspace_bytes(M, N, K, 8)
+        ws = torch.empty(max(wsz, 256), dtype=torch.uint8, device=dev)
+
+        def run(split):
+            def one(i):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record(st)
+                cr._call("convrot_linear", None, 0, xq.data_ptr(), sx.data_ptr(), M, N, K, 256, wq.data_ptr(),
+                         sw.data_ptr(), None, y.data_ptr(), ws.data_ptr() if split else None, wsz if split else 0,
+                         st.cuda_stream)
+                e[1].record(st)
+                return e
+            _, m = timed_loop(one, steps, warmup, torch)
+            return sum(a.elapsed_time(b) for a, b in m) / steps * 1e3
+
+        t_whole = run(False)
+        y_whole = y.clone()
+        t_split = run(True)
+        torch.cuda.synchronize()
+        out["M%d_N%d_K%d" % (M, N, K)] = dict(whole_us=t_whole, split_us=t_split, speedup=t_whole / t_split,
+                                              split_tops=2.0 * M * N * K / (t_split * 1e-6) / 1e12,
+                                              identical=bool(torch.equal(y, y_whole)))
+        log("split-K tail M=%d N=%d K=%d: whole %.1f us, split %.1f us (%.2fx), identical=%s" % (
+            M, N, K, t_whole, t_split, t_whole / t_split, out["M%d_N%d_K%d" % (M, N, K)]["identical"]))
+        del xq, wq, ws
+    return out
+
+
 def copy_probe(torch):
     """Plain device copy of COPY_PROBE_BYTES (5 launches): the calibration kernel for counters."""
     dev = torch.device("cuda:0")
@@ -577,6 +624,8 @@ def main():
         log("stack: median layer %.1f us (%.0f TOP/s) as 7 linears; %.1f us (%.0f TOP/s) with q|k|v and gate|up "
             "as one GEMM each" % (rs["median_layer_us"], rs["median_layer_tops"], rs["fused_median_layer_us"],
                                   rs["fused_median_layer_tops"]))
+    if args.only in ("all", "split"):
+        res["split"] = bench_split(cr, torch, args.steps, args.warmup)
     cpu = None
     if not args.no_cpu_baseline and args.only in ("all", "prefill"):
         cpu = cpu_baseline(wl, torch)
@@ -618,6 +667,8 @@ def main():
         line["w4a4"] = res["w4a4"]
     if "stack" in res:
         line["layer_stack"] = res["stack"]
+    if "split" in res:
+        line["split_k_tail"] = res["split"]
     line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
