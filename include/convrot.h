@@ -53,7 +53,7 @@ typedef enum convrot_status {
     CONVROT_ERR_ALIGN = 4,     /* a pointer violates the alignment rules above                   */
     CONVROT_ERR_DTYPE = 5,     /* unknown dtype code                                             */
     CONVROT_ERR_BITS = 6,      /* bits is not 8 or 4                                             */
-    CONVROT_ERR_WORKSPACE = 7, /* workspace NULL or smaller than convrot_workspace_bytes()       */
+    CONVROT_ERR_WORKSPACE = 7, /* workspace NULL, misaligned or smaller than the call requires  */
     CONVROT_ERR_HIP = 8,       /* a HIP runtime call or kernel launch failed                     */
     CONVROT_ERR_DEVICE = 9     /* the current device is not gfx950                               */
 } convrot_status;
