@@ -175,8 +175,10 @@ int convrot_linear_w4a4_packed(const void *x, int x_dtype, const uint8_t *xq, co
  *   y[m,n] = bf16( sx[m] * sum_j sw[j,n] * (sum_{k in group j} qx[m,k] * cw[n,k]) + bias[n] )
  *   x bf16/fp32 [M, K] rotated and quantized to INT8 into the workspace, or x = NULL and the
  *   caller's xq int8 [M, K] / x_scale fp32 [M] from convrot_quantize_act(bits = 8).
- *   w_packed: the weights in the W4A8 block layout, from convrot_pack_weight_w4a8.
- *   group must be 256, K % 256 == 0, N % 8 == 0, 0 <= M <= CONVROT_W4A8_MAX_M
+ *   w_packed: the weights in the W4A8 block layout, from convrot_pack_weight_w4a8 (group 256) or
+ *   convrot_pack_weight_w4a8_group with this same group.
+ *   group 256, or 128 for a width 256 does not divide (nvfp4-convrot page, section 四, detail 3,
+ *   dynamic group); K % group == 0, N % 8 == 0, 0 <= M <= CONVROT_W4A8_MAX_M
  *   (CONVROT_ERR_SHAPE otherwise; larger batches belong on convrot_linear or convrot_linear_w4a4).
  *   bias fp32 [N] or NULL; y bf16 [M, N].  With x given, the workspace
  *   (convrot_workspace_bytes_w4a8 bytes, 256-byte aligned) holds the INT8 activations; with
@@ -188,21 +190,33 @@ int convrot_linear_w4a8(const void *x, int x_dtype, const int8_t *xq, const floa
 
 /*
  * Offline re-layout of INT4 weights for convrot_linear_w4a8: wq uint8 [N, K/2] and w_scale fp16
- * [K/256, N] from convrot_prepare_weight(bits = 4, group = 256; the decode kernel reads one scale
- * per 256 channels, so weights prepared with group 128 must not be passed) go into one buffer of
+ * [K/256, N] from convrot_prepare_weight(bits = 4, group = 256) go into one buffer of
  * convrot_packed_bytes_w4a8(N, K) bytes (16-byte aligned), ordered the way the decode kernel
- * streams them: per 64-row tile and 256-channel group, the tile's codes (8 KiB, in MFMA operand
+ * streams them: per 64-row tile and 256-channel block, the tile's codes (8 KiB, in MFMA operand
  * order) followed by its 64 scales; rows past N are zero.  The codes and scales are copied
  * unchanged (no requantization).  K % 256 == 0.
  */
 int convrot_pack_weight_w4a8(const uint8_t *wq, const uint16_t *w_scale, int64_t N, int64_t K, void *w_packed,
                              hipStream_t stream);
 
-/* Size of the W4A8 packed weight buffer; 0 on invalid arguments. */
+/* Size of the W4A8 packed weight buffer (group 256); 0 on invalid arguments. */
 size_t convrot_packed_bytes_w4a8(int64_t N, int64_t K);
 
+/*
+ * The same re-layout for either scale group: group 256 as above, or 128 (weights prepared with
+ * group 128, w_scale fp16 [K/128, N]), where each 256-channel block carries two scale sets (the
+ * tile's 64 scales of its lower, then of its upper 128 channels) and, when K % 256 == 128, the
+ * last block's upper half is zero codes with zero scales.  K % group == 0; the buffer holds
+ * convrot_packed_bytes_w4a8_group(N, K, group) bytes.  CONVROT_ERR_GROUP for another group.
+ */
+int convrot_pack_weight_w4a8_group(const uint8_t *wq, const uint16_t *w_scale, int64_t N, int64_t K, int group,
+                                   void *w_packed, hipStream_t stream);
+
+/* Size of the W4A8 packed weight buffer for this group; 0 on invalid arguments. */
+size_t convrot_packed_bytes_w4a8_group(int64_t N, int64_t K, int group);
+
 /* Workspace bytes for convrot_linear_w4a8 at this shape (scratch, like convrot_workspace_bytes);
- * 0 on invalid arguments (M outside [0, CONVROT_W4A8_MAX_M], K not a positive multiple of 256). */
+ * 0 on invalid arguments (M outside [0, CONVROT_W4A8_MAX_M], K not a positive multiple of 128). */
 size_t convrot_workspace_bytes_w4a8(int64_t M, int64_t N, int64_t K);
 
 /*

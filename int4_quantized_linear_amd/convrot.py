@@ -34,6 +34,8 @@ SIGNATURES = {
     "convrot_linear_w4a8": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, SZ, P], I),
     "convrot_pack_weight_w4a8": ([P, P, I64, I64, P, P], I),
     "convrot_packed_bytes_w4a8": ([I64, I64], SZ),
+    "convrot_pack_weight_w4a8_group": ([P, P, I64, I64, I, P, P], I),
+    "convrot_packed_bytes_w4a8_group": ([I64, I64, I], SZ),
     "convrot_workspace_bytes_w4a8": ([I64, I64, I64], SZ),
     "convrot_gemm_i8_i32": ([P, P, I64, I64, I64, P, P, SZ, P], I),
     "convrot_gemm_i4_i32": ([P, P, I64, I64, I64, P, P, SZ, P], I),
@@ -216,18 +218,22 @@ def workspace_bytes_w4a8(M: int, N: int, K: int) -> int:
     return int(load().convrot_workspace_bytes_w4a8(M, N, K))
 
 
-def packed_bytes_w4a8(N: int, K: int) -> int:
-    return int(load().convrot_packed_bytes_w4a8(N, K))
+def packed_bytes_w4a8(N: int, K: int, group: int = 256) -> int:
+    return int(load().convrot_packed_bytes_w4a8_group(N, K, group))
 
 
-def pack_weight_w4a8(wq: torch.Tensor, w_scale: torch.Tensor) -> torch.Tensor:
-    """Re-lay out INT4 weights (prepare_weight(bits=4): wq uint8 [N, K/2], w_scale fp16 [K/256, N])
-    into the W4A8 decode kernel's block layout (a flat uint8 buffer)."""
+def pack_weight_w4a8(wq: torch.Tensor, w_scale: torch.Tensor, group: int = 256) -> torch.Tensor:
+    """Re-lay out INT4 weights (prepare_weight(bits=4): wq uint8 [N, K/2], w_scale fp16
+    [K/group, N], group 256 or 128) into the W4A8 decode kernel's block layout (a flat uint8
+    buffer); linear_w4a8 must then be called with the same group."""
     _check_dev(wq, w_scale)
     N, Kh = wq.shape
     K = 2 * Kh
-    out = torch.empty(max(packed_bytes_w4a8(N, K), 16), dtype=torch.uint8, device=wq.device)
-    _call("convrot_pack_weight_w4a8", _ptr(wq), _ptr(w_scale), N, K, _ptr(out), _stream(wq.device))
+    out = torch.empty(max(packed_bytes_w4a8(N, K, group), 16), dtype=torch.uint8, device=wq.device)
+    if group == 256:
+        _call("convrot_pack_weight_w4a8", _ptr(wq), _ptr(w_scale), N, K, _ptr(out), _stream(wq.device))
+    else:
+        _call("convrot_pack_weight_w4a8_group", _ptr(wq), _ptr(w_scale), N, K, group, _ptr(out), _stream(wq.device))
     return out
 
 

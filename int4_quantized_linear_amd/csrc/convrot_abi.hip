@@ -357,30 +357,56 @@ int convrot_linear_w4a4_packed(const void *x, int x_dtype, const uint8_t *xq, co
 
 size_t convrot_workspace_bytes_w4a8(int64_t M, int64_t N, int64_t K)
 {
-    if (M < 0 || M > CONVROT_W4A8_MAX_M || N < 0 || K <= 0 || K % 256 || K > CONVROT_MAX_K) return 0;
+    if (M < 0 || M > CONVROT_W4A8_MAX_M || N < 0 || K <= 0 || K % 128 || K > CONVROT_MAX_K) return 0;
     return ws_layout_w4a8(M, K).total;
 }
 
-size_t convrot_packed_bytes_w4a8(int64_t N, int64_t K)
+size_t convrot_packed_bytes_w4a8_group(int64_t N, int64_t K, int group)
 {
-    if (N < 0 || N >= ((int64_t)1 << 31) || K <= 0 || K % 256 || K > CONVROT_MAX_K) return 0;
-    return convrot::w4a8_packed_bytes(N, (int)K);
+    if (N < 0 || N >= ((int64_t)1 << 31) || K <= 0 || K > CONVROT_MAX_K || (group != 256 && group != 128) ||
+        K % group)
+        return 0;
+    return convrot::w4a8_packed_bytes(N, (int)K, group);
 }
 
-int convrot_pack_weight_w4a8(const uint8_t *wq, const uint16_t *w_scale, int64_t N, int64_t K, void *w_packed,
-                             hipStream_t stream)
+size_t convrot_packed_bytes_w4a8(int64_t N, int64_t K) { return convrot_packed_bytes_w4a8_group(N, K, 256); }
+
+} // extern "C"
+
+namespace {
+
+int pack_w4a8(const char *who, const uint8_t *wq, const uint16_t *w_scale, int64_t N, int64_t K, int group,
+              void *w_packed, hipStream_t stream)
 {
-    const char *who = "convrot_pack_weight_w4a8";
-    int rc = check_shape(N, 1, K, 256, who);
+    int rc = check_shape(N, 1, K, group, who);
     if (rc) return rc;
-    if (K % 256) return fail(CONVROT_ERR_GROUP, "%s: K=%lld must be a multiple of 256", who, (long long)K);
+    if ((group != 256 && group != 128) || K % group)
+        return fail(CONVROT_ERR_GROUP, "%s: W4A8 needs group 256 or 128 dividing K (group=%d, K=%lld)", who, group,
+                    (long long)K);
     if (N == 0) return CONVROT_OK;
     if (!wq || !w_scale || !w_packed) return fail(CONVROT_ERR_NULL, "%s: wq, w_scale and w_packed must be non-NULL", who);
     if (!aligned(wq, 16) || !aligned(w_scale, 2) || !aligned(w_packed, 16))
         return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
     if ((rc = check_device())) return rc;
-    return hip_status(convrot::launch_pack_w4a8(wq, w_scale, N, (int)K, static_cast<uint8_t *>(w_packed), stream),
-                      "pack_w4a8");
+    return hip_status(
+        convrot::launch_pack_w4a8(wq, w_scale, N, (int)K, group, static_cast<uint8_t *>(w_packed), stream),
+        "pack_w4a8");
+}
+
+} // namespace
+
+extern "C" {
+
+int convrot_pack_weight_w4a8(const uint8_t *wq, const uint16_t *w_scale, int64_t N, int64_t K, void *w_packed,
+                             hipStream_t stream)
+{
+    return pack_w4a8("convrot_pack_weight_w4a8", wq, w_scale, N, K, 256, w_packed, stream);
+}
+
+int convrot_pack_weight_w4a8_group(const uint8_t *wq, const uint16_t *w_scale, int64_t N, int64_t K, int group,
+                                   void *w_packed, hipStream_t stream)
+{
+    return pack_w4a8("convrot_pack_weight_w4a8_group", wq, w_scale, N, K, group, w_packed, stream);
 }
 
 int convrot_linear_w4a8(const void *x, int x_dtype, const int8_t *xq, const float *x_scale, int64_t M, int64_t N,
@@ -390,7 +416,9 @@ int convrot_linear_w4a8(const void *x, int x_dtype, const int8_t *xq, const floa
     const char *who = "convrot_linear_w4a8";
     int rc = check_shape(M, N, K, group, who);
     if (rc) return rc;
-    if (group != 256 || K % 256) return fail(CONVROT_ERR_GROUP, "%s: W4A8 needs group 256 and K %% 256 == 0", who);
+    if ((group != 256 && group != 128) || K % group)
+        return fail(CONVROT_ERR_GROUP, "%s: W4A8 needs group 256 or 128 dividing K (group=%d, K=%lld); the weights "
+                    "must be packed with the same group", who, group, (long long)K);
     if (M > CONVROT_W4A8_MAX_M)
         return fail(CONVROT_ERR_SHAPE, "%s: M=%lld tokens; the W4A8 kernel is the decode path (M <= %d)", who,
                     (long long)M, CONVROT_W4A8_MAX_M);
@@ -420,7 +448,7 @@ int convrot_linear_w4a8(const void *x, int x_dtype, const int8_t *xq, const floa
         x_scale = sx;
     }
     return hip_status(convrot::launch_gemv_w4a8(xq, x_scale, static_cast<const uint8_t *>(w_packed), bias, y, M, N,
-                                                (int)K, stream),
+                                                (int)K, group, stream),
                       "gemv_w4a8");
 }
 

@@ -43,6 +43,13 @@ constexpr int RBW = 4;                   // 16-row blocks per tile
 constexpr int RT = 16 * RBW;             // rows per tile
 constexpr int CODE_BYTES = RT * GS / 2;  // 8 KiB
 constexpr int BS = CODE_BYTES + 2 * RT;  // + the tile's 64 fp16 scales
+// 128-channel scale groups (the dynamic group of a width 256 does not divide): a block keeps
+// 256 channels and carries two scale sets, half i's at CODE_BYTES + 128 i (the pieces (b, i)
+// are exactly channels 128 i .. 128 i + 127 of the block); when K % 256 == 128 the last block's
+// upper half is zero codes with zero scales.
+constexpr int BS128 = CODE_BYTES + 4 * RT;
+template <bool G128>
+constexpr int block_bytes() { return G128 ? BS128 : BS; }
 constexpr int TARGET_WAVES = 640;       // about 2.5 wavefronts per CU in all
 constexpr int MIN_GROUPS = 5;            // per wavefront, to amortise its ramp-up and drain
 constexpr uint32_t OOB = 0x80000000u;
@@ -53,19 +60,21 @@ typedef __attribute__((address_space(3))) void lds_void;
 // ------------------------------------------------------------------ packing
 
 // One thread per 16-byte code piece or per 8-byte scale quad of a block.
+template <bool G128>
 __global__ void __launch_bounds__(256) pack_w4a8_kernel(const uint8_t *__restrict__ wq, const uint16_t *__restrict__ sw,
                                                         uint8_t *__restrict__ out, int64_t N, int K, int64_t nblocks)
 {
-    const int G = K / GS;
+    const int G = (K + GS - 1) / GS;
     const int Kh = K / 2;
-    const int per_block = CODE_BYTES / 16 + RT / 4;      // 512 pieces + 16 scale quads
+    constexpr int NSC = G128 ? 2 : 1;                    // scale sets per block
+    const int per_block = CODE_BYTES / 16 + NSC * RT / 4;   // 512 pieces + 16 scale quads per set
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= nblocks * per_block) return;
     const int64_t blk = idx / per_block;
     const int piece = (int)(idx % per_block);
     const int64_t t = blk / G;
     const int j = (int)(blk % G);
-    uint8_t *dst = out + blk * BS;
+    uint8_t *dst = out + blk * block_bytes<G128>();
     if (piece < CODE_BYTES / 16) {
         const int bi = piece >> 6, l = piece & 63;
         const int b = bi >> 1, i = bi & 1;
@@ -78,8 +87,8 @@ __global__ void __launch_bounds__(256) pack_w4a8_kernel(const uint8_t *__restric
                 const int kk = 2 * i + h;
                 uint32_t nib[16];
                 for (int s = 0; s < 16; ++s) {
-                    const int k = 64 * kk + 16 * q + s;  // channel within the group
-                    const uint8_t byte = src[k >> 1];
+                    const int k = 64 * kk + 16 * q + s;  // channel within the block
+                    const uint8_t byte = j * GS + k < K ? src[k >> 1] : (uint8_t)0;   // past K: zero
                     nib[s] = (k & 1) ? (byte >> 4) : (byte & 15u);
                 }
                 uint32_t dA = 0, dB = 0;
@@ -94,14 +103,16 @@ __global__ void __launch_bounds__(256) pack_w4a8_kernel(const uint8_t *__restric
         uint32_t *o = reinterpret_cast<uint32_t *>(dst + 1024 * bi + 16 * l);
         for (int u = 0; u < 4; ++u) o[u] = d[u];
     } else {
-        const int sq = piece - CODE_BYTES / 16;          // 0..15: (q, b)
-        const int q = sq >> 2, b = sq & 3;
+        const int sq = piece - CODE_BYTES / 16;          // (set, q, b)
+        const int set = sq >> 4, q = (sq >> 2) & 3, b = sq & 3;
+        const int gi = NSC * j + set;                    // scale group index
+        const bool gok = gi < K / (GS / NSC);
         uint16_t v4[4];
         for (int v = 0; v < 4; ++v) {
             const int64_t row = t * RT + 16 * b + 4 * q + v;
-            v4[v] = row < N ? sw[(int64_t)j * N + row] : (uint16_t)0;
+            v4[v] = (row < N && gok) ? sw[(int64_t)gi * N + row] : (uint16_t)0;
         }
-        uint16_t *o = reinterpret_cast<uint16_t *>(dst + CODE_BYTES + 32 * q + 8 * b);
+        uint16_t *o = reinterpret_cast<uint16_t *>(dst + CODE_BYTES + (2 * RT) * set + 32 * q + 8 * b);
         for (int v = 0; v < 4; ++v) o[v] = v4[v];
     }
 }
@@ -118,10 +129,10 @@ struct W4A8Params {
     int M, K;
 };
 
-template <int RB>
+template <int RB, bool G128>
 struct Chunk {
-    v4i wa[RB][2];           // code pieces (b0 + b, i)
-    uint32_t sc[2 * RB];     // fp16 scales of rows 16(b0 + b) + 4q + v: half v of dword 2b + v/2
+    v4i wa[RB][2];                       // code pieces (b0 + b, i)
+    uint32_t sc[G128 ? 2 : 1][2 * RB];   // scale set s: fp16 of rows 16(b0 + b) + 4q + v, half v of dword 2b + v/2
 };
 
 __device__ __forceinline__ v4i widen_step(uint32_t dA, uint32_t dB)
@@ -145,11 +156,13 @@ constexpr int MAX_NW = 8;                // wavefronts per workgroup
 // contiguous run of groups.  Per group it loads its RB code pieces and the scale bytes into a
 // register ring and the group's 16 token rows into its own LDS ring (load-to-LDS, 1 KiB per
 // instruction, token t keeping 16-byte chunk c at c ^ t; tokens >= M arrive as zeros).
-template <int RB>
+template <int RB, bool G128>
 __global__ void __launch_bounds__(64 * MAX_NW) gemv_w4a8_kernel(W4A8Params p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr int LPC = 2 * RB + (RB + 1) / 2 + 4;       // loads per chunk, token loads last
+    constexpr int NSC = G128 ? 2 : 1;
+    constexpr int BSZ = block_bytes<G128>();
+    constexpr int LPC = 2 * RB + NSC * ((RB + 1) / 2) + 4;   // loads per chunk, token loads last
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nw = blockDim.x >> 6;
@@ -157,8 +170,8 @@ __global__ void __launch_bounds__(64 * MAX_NW) gemv_w4a8_kernel(W4A8Params p)
     const int64_t t64 = n0 / RT;                         // packed 64-row tile
     const int b0 = (int)(n0 % RT) / 16;                  // first row block inside it
     const int K = p.K;
-    const int G = K / GS;
-    const int g_beg = G * w / nw;                        // nw <= G: every run has a group
+    const int G = (K + GS - 1) / GS;                     // 256-channel blocks
+    const int g_beg = G * w / nw;                        // nw <= G: every run has a block
     const int g_end = G * (w + 1) / nw;
     const int n = g_end - g_beg;
     const int r = lane & 15, q = lane >> 4;
@@ -184,7 +197,7 @@ __global__ void __launch_bounds__(64 * MAX_NW) gemv_w4a8_kernel(W4A8Params p)
     }
 
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(p.wp + t64 * G * (int64_t)BS), (short)0, NUM_RECORDS, 0x00020000);
+        const_cast<uint8_t *>(p.wp + t64 * G * (int64_t)BSZ), (short)0, NUM_RECORDS, 0x00020000);
     const __amdgpu_buffer_rsrc_t rx =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(p.xq), (short)0, NUM_RECORDS, 0x00020000);
     uint8_t *xs = smem + w * (D * XSTAGE);               // this wavefront's token ring
@@ -194,10 +207,10 @@ __global__ void __launch_bounds__(64 * MAX_NW) gemv_w4a8_kernel(W4A8Params p)
     // chunk c of this wavefront = group g_beg + c.  Chunks past the run load nothing: bit 31 set
     // in an offset makes it out of range (zeros, no memory access).  Plain arithmetic rather than
     // selects, which the compiler would turn into branches around the loads.
-    auto load = [&](Chunk<RB> &ch, int slot, int c) {
+    auto load = [&](Chunk<RB, G128> &ch, int slot, int c) {
         const uint32_t dead = (uint32_t)(c >= n) << 31;
         const int g = g_beg + c;
-        const uint32_t blk = (uint32_t)g * (uint32_t)BS;
+        const uint32_t blk = (uint32_t)g * (uint32_t)BSZ;
 #pragma unroll
         for (int b = 0; b < RB; ++b)
 #pragma unroll
@@ -205,24 +218,29 @@ __global__ void __launch_bounds__(64 * MAX_NW) gemv_w4a8_kernel(W4A8Params p)
                 ch.wa[b][i] = __builtin_bit_cast(
                     v4i, __builtin_amdgcn_raw_buffer_load_b128(
                              rw, (blk + 1024 * (2 * (b0 + b) + i) + 16 * lane) | dead, 0, 2));
-        // this lane's scale bytes [32q + 8 b0, + 8 RB) of the tile's 128
-        const uint32_t so = (blk + CODE_BYTES + 32 * q + 8 * b0) | dead;
-        if constexpr (RB == 1) {
-            const v2u v = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rw, so, 0, 0));
-            ch.sc[0] = v[0];
-            ch.sc[1] = v[1];
-        } else {
+        // this lane's scale bytes [32q + 8 b0, + 8 RB) of each of the block's scale sets (128 bytes each)
 #pragma unroll
-            for (int h = 0; h < RB / 2; ++h) {
-                const v4u v = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rw, so + 16 * h, 0, 0));
+        for (int st = 0; st < NSC; ++st) {
+            const uint32_t so = (blk + CODE_BYTES + 2 * RT * st + 32 * q + 8 * b0) | dead;
+            if constexpr (RB == 1) {
+                const v2u v = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rw, so, 0, 0));
+                ch.sc[st][0] = v[0];
+                ch.sc[st][1] = v[1];
+            } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ch.sc[4 * h + e] = v[e];
+                for (int h = 0; h < RB / 2; ++h) {
+                    const v4u v = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rw, so + 16 * h, 0, 0));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ch.sc[st][4 * h + e] = v[e];
+                }
             }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int t = 4 * j + tx;
-            const uint32_t off = (uint32_t)(t * K + g * GS + 16 * (px ^ t)) | dead | ((uint32_t)(t >= M) << 31);
+            // channels past K (the upper half of the last block when K % 256 == 128) load nothing
+            const int kc = g * GS + 16 * (px ^ t);
+            const uint32_t off = (uint32_t)(t * K + kc) | dead | ((uint32_t)(t >= M) << 31) | ((uint32_t)(kc >= K) << 31);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(xs + slot * XSTAGE + 1024 * j), 16, off, 0, 0, 0);
         }
     };
@@ -233,32 +251,38 @@ __global__ void __launch_bounds__(64 * MAX_NW) gemv_w4a8_kernel(W4A8Params p)
 #pragma unroll
         for (int v = 0; v < 4; ++v) facc[b][v] = 0.0f;
 
-    auto compute = [&](const Chunk<RB> &ch, int slot) {
+    auto compute = [&](const Chunk<RB, G128> &ch, int slot) {
         // the token rows of this chunk have landed once at most the next chunk's loads remain
         __builtin_amdgcn_s_waitcnt(waitcnt_vm((D - 1) * LPC));
         const uint8_t *xst = xs + slot * XSTAGE + r * GS;
         v4i iacc[RB];
+        // fold: facc += float(iacc) * s_w of scale set st, per output
+        auto fold = [&](int st) {
+#pragma unroll
+            for (int b = 0; b < RB; ++b)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const unsigned short h = (unsigned short)(ch.sc[st][2 * b + (v >> 1)] >> (16 * (v & 1)));
+                    facc[b][v] = __builtin_fmaf((float)iacc[b][v], (float)__ushort_as_half(h), facc[b][v]);
+                }
+        };
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            // token r, chunk 4kk + q of the group (16 channels 64kk + 16q ..)
+            // token r, chunk 4kk + q of the block (16 channels 64kk + 16q ..)
             const v4i xb = *reinterpret_cast<const v4i *>(xst + 16 * ((4 * kk + q) ^ r));
+            const bool first = G128 ? (kk & 1) == 0 : kk == 0;   // a scale group's first K-step
 #pragma unroll
             for (int b = 0; b < RB; ++b) {
                 const v4i &src = ch.wa[b][kk >> 1];
                 const v4i a = widen_step((uint32_t)src[2 * (kk & 1)], (uint32_t)src[2 * (kk & 1) + 1]);
-                iacc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xb, kk ? iacc[b] : v4i{}, 0, 0, 0);
+                iacc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xb, first ? v4i{} : iacc[b], 0, 0, 0);
             }
+            if (G128 && kk == 1) fold(0);                // channels 0..127 of the block: scale set 0
         }
-#pragma unroll
-        for (int b = 0; b < RB; ++b)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const unsigned short h = (unsigned short)(ch.sc[2 * b + (v >> 1)] >> (16 * (v & 1)));
-                facc[b][v] = __builtin_fmaf((float)iacc[b][v], (float)__ushort_as_half(h), facc[b][v]);
-            }
+        fold(NSC - 1);
     };
 
-    Chunk<RB> ring[D];
+    Chunk<RB, G128> ring[D];
 #pragma unroll
     for (int j = 0; j < D; ++j) {
         load(ring[j], j, j);
@@ -328,45 +352,54 @@ Plan plan(int64_t N, int K)
     pl.rb = N >= 4096 ? 2 : 1;
     pl.tiles = (N + 16 * pl.rb - 1) / (16 * pl.rb);
     int64_t nw = (TARGET_WAVES + pl.tiles - 1) / pl.tiles;
-    const int G = K / GS;
+    const int G = (K + GS - 1) / GS;
     if (nw > G / MIN_GROUPS) nw = G / MIN_GROUPS;
     if (nw > MAX_NW) nw = MAX_NW;
     pl.nw = nw < 1 ? 1 : (int)nw;
     return pl;
 }
 
-template <int RB>
+template <int RB, bool G128>
 hipError_t launch(const W4A8Params &p, const Plan &pl, hipStream_t stream)
 {
     const size_t lds = (size_t)pl.nw * D * XSTAGE;
-    hipLaunchKernelGGL((gemv_w4a8_kernel<RB>), dim3((unsigned)pl.tiles), dim3(64 * pl.nw), lds, stream, p);
+    hipLaunchKernelGGL((gemv_w4a8_kernel<RB, G128>), dim3((unsigned)pl.tiles), dim3(64 * pl.nw), lds, stream, p);
     return hipGetLastError();
 }
 
 } // namespace
 
-size_t w4a8_packed_bytes(int64_t N, int K)
+size_t w4a8_packed_bytes(int64_t N, int K, int group)
 {
     const int64_t tiles = (N + RT - 1) / RT;
+    if (group == 128) return (size_t)(tiles * ((K + GS - 1) / GS) * BS128);
     return (size_t)(tiles * (K / GS) * BS);
 }
 
-hipError_t launch_pack_w4a8(const uint8_t *wq, const uint16_t *sw, int64_t N, int K, uint8_t *out, hipStream_t stream)
+hipError_t launch_pack_w4a8(const uint8_t *wq, const uint16_t *sw, int64_t N, int K, int group, uint8_t *out,
+                            hipStream_t stream)
 {
-    const int64_t nblocks = (N + RT - 1) / RT * (K / GS);
-    const int64_t threads = nblocks * (CODE_BYTES / 16 + RT / 4);
+    if (group != 256 && group != 128) return hipErrorInvalidValue;
+    if (K % group) return hipErrorInvalidValue;
+    const bool g128 = group == 128;
+    const int64_t nblocks = (N + RT - 1) / RT * ((K + GS - 1) / GS);
+    const int64_t threads = nblocks * (CODE_BYTES / 16 + (g128 ? 2 : 1) * RT / 4);
     if (threads == 0) return hipSuccess;
-    hipLaunchKernelGGL(pack_w4a8_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, wq, sw, out, N,
-                       K, nblocks);
+    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    if (g128)
+        hipLaunchKernelGGL(pack_w4a8_kernel<true>, grid, block, 0, stream, wq, sw, out, N, K, nblocks);
+    else
+        hipLaunchKernelGGL(pack_w4a8_kernel<false>, grid, block, 0, stream, wq, sw, out, N, K, nblocks);
     return hipGetLastError();
 }
 
 int gemv_w4a8_waves(int64_t N, int K) { return plan(N, K).nw; }
 
 hipError_t launch_gemv_w4a8(const int8_t *xq, const float *sx, const uint8_t *wp, const float *bias, void *y,
-                            int64_t M, int64_t N, int K, hipStream_t stream)
+                            int64_t M, int64_t N, int K, int group, hipStream_t stream)
 {
     if (M <= 0 || N <= 0) return hipSuccess;
+    if ((group != 256 && group != 128) || K % group) return hipErrorInvalidValue;
     W4A8Params p;
     p.xq = xq;
     p.wp = wp;
@@ -377,8 +410,8 @@ hipError_t launch_gemv_w4a8(const int8_t *xq, const float *sx, const uint8_t *wp
     p.M = (int)M;
     p.K = K;
     const Plan pl = plan(N, K);
-    if (pl.rb == 2) return launch<2>(p, pl, stream);
-    return launch<1>(p, pl, stream);
+    if (group == 128) return pl.rb == 2 ? launch<2, true>(p, pl, stream) : launch<1, true>(p, pl, stream);
+    return pl.rb == 2 ? launch<2, false>(p, pl, stream) : launch<1, false>(p, pl, stream);
 }
 
 } // namespace convrot

@@ -46,12 +46,14 @@ hipError_t launch_gemm_w4a4(const uint8_t *xq, const uint8_t *wq, bool w_tiled, 
 
 // W4A8 decode linear (M <= 16): y = bf16(sx[m] * sum_g sw[g,n] * (qx . cw over group g) + bias[n])
 // with INT8 tokens and the weights in the W4A8 block layout (codes and fp16 group scales), made
-// once by launch_pack_w4a8 from packed INT4 [N, K/2] and scales [K/256, N]; N % 8 == 0.
+// once by launch_pack_w4a8 from packed INT4 [N, K/2] and scales [K/group, N] (group 256, or 128
+// with two scale sets per 256-channel block); N % 8 == 0.
 // No scratch memory: K is split only among the wavefronts of one workgroup.
-size_t w4a8_packed_bytes(int64_t N, int K);
-hipError_t launch_pack_w4a8(const uint8_t *wq, const uint16_t *sw, int64_t N, int K, uint8_t *out, hipStream_t stream);
+size_t w4a8_packed_bytes(int64_t N, int K, int group);
+hipError_t launch_pack_w4a8(const uint8_t *wq, const uint16_t *sw, int64_t N, int K, int group, uint8_t *out,
+                            hipStream_t stream);
 int gemv_w4a8_waves(int64_t N, int K);
 hipError_t launch_gemv_w4a8(const int8_t *xq, const float *sx, const uint8_t *wp, const float *bias, void *y,
-                            int64_t M, int64_t N, int K, hipStream_t stream);
+                            int64_t M, int64_t N, int K, int group, hipStream_t stream);
 
 } // namespace convrot

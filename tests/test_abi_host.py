@@ -38,6 +38,7 @@ def test_header_declares_the_boundary():
     for name in ("convrot_prepare_weight", "convrot_quantize_act", "convrot_linear", "convrot_linear_w4a4",
                  "convrot_pack_weight_w4a4", "convrot_packed_bytes_w4a4", "convrot_linear_w4a4_packed",
                  "convrot_linear_w4a8", "convrot_pack_weight_w4a8", "convrot_packed_bytes_w4a8",
+                 "convrot_pack_weight_w4a8_group", "convrot_packed_bytes_w4a8_group",
                  "convrot_workspace_bytes", "convrot_workspace_bytes_w4a8",
                  "convrot_gemm_i8_i32", "convrot_gemm_i4_i32", "convrot_dynamic_group", "convrot_last_error",
                  "convrot_status_string"):
@@ -119,6 +120,17 @@ def test_dynamic_group_matches_the_oracle(lib):
     assert cr.dynamic_group(2688) == 128
     with pytest.raises(cr.ConvRotError):
         cr.dynamic_group(512, 3)
+
+
+def test_packed_bytes_w4a8_group(lib):
+    pb = lib.convrot_packed_bytes_w4a8_group
+    assert pb(64, 512, 64) == 0 and pb(64, 384, 256) == 0 and pb(64, 320, 128) == 0 and pb(-1, 512, 128) == 0
+    for N, K in [(64, 256), (1000, 5376)]:
+        assert pb(N, K, 256) == lib.convrot_packed_bytes_w4a8(N, K)
+    # group 128: 256-channel blocks (the last one half empty when K % 256 == 128), each with two
+    # scale sets of 128 bytes
+    for N, K in [(64, 128), (64, 384), (200, 2688), (1024, 5120)]:
+        assert pb(N, K, 128) == -(-N // 64) * -(-K // 256) * (8192 + 256), (N, K)
 
 
 def test_packed_bytes_w4a8(lib):
@@ -262,7 +274,8 @@ CASES = [
     # W4A8 decode linear and its weight re-layout
     ("convrot_linear_w4a8", w48_args(M=17), "CONVROT_ERR_SHAPE"),
     ("convrot_linear_w4a8", w48_args(K=100), "CONVROT_ERR_SHAPE"),
-    ("convrot_linear_w4a8", w48_args(group=128), "CONVROT_ERR_GROUP"),
+    ("convrot_linear_w4a8", w48_args(group=512), "CONVROT_ERR_GROUP"),
+    ("convrot_linear_w4a8", w48_args(K=384), "CONVROT_ERR_SHAPE"),           # group 256 must divide K
     ("convrot_linear_w4a8", w48_args(K=320, group=64), "CONVROT_ERR_GROUP"),
     ("convrot_linear_w4a8", w48_args(wp=None), "CONVROT_ERR_NULL"),
     ("convrot_linear_w4a8", w48_args(x=None, xq=A), "CONVROT_ERR_NULL"),
@@ -281,6 +294,10 @@ CASES = [
     ("convrot_pack_weight_w4a8", (A, C, 64, 512, None, None), "CONVROT_ERR_NULL"),
     ("convrot_pack_weight_w4a8", (A, C + 1, 64, 512, B, None), "CONVROT_ERR_ALIGN"),
     ("convrot_pack_weight_w4a8", (A, C, 64, 512, B + 8, None), "CONVROT_ERR_ALIGN"),
+    ("convrot_pack_weight_w4a8_group", (A, C, 64, 512, 64, B, None), "CONVROT_ERR_GROUP"),
+    ("convrot_pack_weight_w4a8_group", (A, C, 64, 384, 256, B, None), "CONVROT_ERR_SHAPE"),
+    ("convrot_pack_weight_w4a8_group", (None, C, 64, 384, 128, B, None), "CONVROT_ERR_NULL"),
+    ("convrot_pack_weight_w4a8_group", (A, C + 1, 64, 384, 128, B, None), "CONVROT_ERR_ALIGN"),
     # integer cores
     ("convrot_gemm_i8_i32", (A, B, 32, 256, 96, C, None, 0, None), "CONVROT_ERR_SHAPE"),
     ("convrot_gemm_i8_i32", (A, B, 32, 1 << 24, 512, C, None, 0, None), "CONVROT_ERR_SHAPE"),

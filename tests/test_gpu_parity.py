@@ -189,8 +189,10 @@ def test_linear_dynamic_group_adaln_width(cr):
     for M, N in [(12, 1000), (300, 2048)]:
         P.say("dynamic-group W4A4 M=%d N=%d K=%d g=%d" % (M, N, K, g))
         _w4a4_case(cr, *workloads.ragged_case(M, K, N, seed=12), g)
-    # the W4A8 decode path keeps 256-channel groups: its re-layout rejects the width (256 does
-    # not divide it), nothing is silently regrouped
+    # and the W4A8 decode path (two scale sets per 256-channel block, a zero upper half in the
+    # last one); the group-256 re-layout still rejects the width, nothing is silently regrouped
+    P.say("dynamic-group W4A8 M=12 N=1000 K=%d g=%d" % (K, g))
+    _w4a8_case(cr, *workloads.ragged_case(12, K, 1000, seed=13), "w4a8 dynamic-group y", g=g)
     w4 = workloads.gaussian_weights(64, K, cfg=94).to(DEV)
     wq4, ws4 = cr.prepare_weight(w4, g, 4)
     assert ws4.shape == (K // g, 64)
@@ -513,24 +515,24 @@ def test_linear_w4a4_full_size_sampled(cr):
 
 # ------------------------------------------------------------------ W4A8 (decode, M <= 16)
 
-def _w4a8_case(cr, x, w, b, what):
+def _w4a8_case(cr, x, w, b, what, g=256):
     xd, wd = x.to(DEV), w.to(DEV)
     bd = None if b is None else b.to(DEV)
     N = w.shape[0]
-    wq, ws = cr.prepare_weight(wd, 256, 4)
-    wp = cr.pack_weight_w4a8(wq, ws)
-    y = cr.linear_w4a8(xd, wp, N, bd)
-    xq, xs = cr.quantize_act(xd, 256, 8)
-    y2 = cr.linear_w4a8(None, wp, N, bd, xq=xq, x_scale=xs)
+    wq, ws = cr.prepare_weight(wd, g, 4)
+    wp = cr.pack_weight_w4a8(wq, ws, g)
+    y = cr.linear_w4a8(xd, wp, N, bd, group=g)
+    xq, xs = cr.quantize_act(xd, g, 8)
+    y2 = cr.linear_w4a8(None, wp, N, bd, group=g, xq=xq, x_scale=xs)
     torch.cuda.synchronize()
     bn = None if b is None else b.numpy()
-    ref = orc.linear_w4a8(_x64(x), _x64(w), bn, 256)
+    ref = orc.linear_w4a8(_x64(x), _x64(w), bn, g)
     P.check_codes(_np(xq), ref["qx"], "qx")
     P.check_scales_f32(_np(xs), ref["sx"], "sx")
     P.check_scales_f16(_np(ws).T, ref["sw"], "sw16")
     P.check_codes(orc.unpack_i4(_np(wq)), ref["cw"], "int4 weight codes", rate=1e-3)
     # exact integer group sums on the GPU's own codes: only fp32 rounding of the scaled sums differs
-    yown = orc.linear_w4a8_codes(_np(xq), _np(xs), orc.unpack_i4(_np(wq)), _np(ws).T, bn, 256)
+    yown = orc.linear_w4a8_codes(_np(xq), _np(xs), orc.unpack_i4(_np(wq)), _np(ws).T, bn, g)
     P.check_y(_x64(y), yown, what + " (own codes)", strict_frac=1e-4)
     P.check_y(_x64(y), ref["y"], what + " (oracle codes)", strict_frac=2e-2)
     assert torch.equal(y, y2), "pre-quantized path differs from the fused path"
@@ -551,6 +553,18 @@ def test_linear_w4a8_parity(cr, M, N, K):
     _w4a8_case(cr, x, w, b, "w4a8 y")
 
 
+# 128-channel scale groups (the dynamic group): one half block (K = 128), K % 256 == 128 (a
+# zero upper half in the last block), K % 256 == 0, ragged rows, several wavefront splits
+W4A8_G128_CASES = [(5, 64, 128), (3, 200, 384), (16, 520, 2688), (12, 1000, 5120), (7, 136, 25600 + 128)]
+
+
+@pytest.mark.parametrize("M,N,K", W4A8_G128_CASES)
+def test_linear_w4a8_group128_parity(cr, M, N, K):
+    P.say("linear_w4a8 g=128 M=%d N=%d K=%d" % (M, N, K))
+    x, w, b = workloads.ragged_case(M, K, N, seed=8)
+    _w4a8_case(cr, x, w, b, "w4a8 g128 y", g=128)
+
+
 @pytest.mark.parametrize("K,N", workloads.DECODE_SHAPES)
 def test_linear_w4a8_decode_shapes(cr, K, N):
     P.say("w4a8 decode M=12 K=%d N=%d" % (K, N))
@@ -558,17 +572,22 @@ def test_linear_w4a8_decode_shapes(cr, K, N):
     _w4a8_case(cr, x, w, None, "w4a8 decode y")
 
 
-def _unpack_w4a8_layout(buf: np.ndarray, N: int, K: int):
+def _unpack_w4a8_layout(buf: np.ndarray, N: int, K: int, g: int = 256):
     """CPU reading of the W4A8 block layout as the header and kernel source describe it:
-    per 64-row tile t and group j a block of 8320 bytes at (t*G + j)*8320; piece (b, i) at
-    1024*(2b+i), lane l = (r, q) at 16*l holds K-steps 2i, 2i+1 of row 16b+r as dwords (dA, dB);
-    dA byte u = channel 64kk+16q+u (high nibble) | channel 64kk+16q+4+u (low nibble), dB the
-    same for +8, +12; scales at 8192 + 32q + 8b + 2v for row 16b+4q+v."""
-    G = K // 256
+    per 64-row tile t and 256-channel block j a block of BS bytes at (t*G + j)*BS (BS = 8320 for
+    group 256, 8448 for group 128); piece (b, i) at 1024*(2b+i), lane l = (r, q) at 16*l holds
+    K-steps 2i, 2i+1 of row 16b+r as dwords (dA, dB); dA byte u = channel 64kk+16q+u (high
+    nibble) | channel 64kk+16q+4+u (low nibble), dB the same for +8, +12; scale set s (one for
+    group 256; for group 128 s = 0 the block's lower, s = 1 its upper 128 channels) at
+    8192 + 128s + 32q + 8b + 2v for row 16b+4q+v.  Returns the codes over all blocks' channels
+    (G*256, past K included) and the scales [rows, K/g]."""
+    G = -(-K // 256)
     T = -(-N // 64)
-    blocks = buf[: T * G * 8320].reshape(T, G, 8320)
-    codes = np.zeros((T * 64, K), np.int8)
-    scales = np.zeros((T * 64, G), np.uint16)
+    nsc = 2 if g == 128 else 1
+    BS = 8192 + 128 * nsc
+    blocks = buf[: T * G * BS].reshape(T, G, BS)
+    codes = np.zeros((T * 64, G * 256), np.int8)
+    scales = np.zeros((T * 64, G * nsc), np.uint16)
     def s4(x):
         return ((x.astype(np.int16) ^ 8) - 8).astype(np.int8)
     for b in range(4):
@@ -586,28 +605,34 @@ def _unpack_w4a8_layout(buf: np.ndarray, N: int, K: int):
                                 rows = np.arange(T)[:, None] * 64 + 16 * b + np.arange(16)[None, :]
                                 codes[rows, 256 * j + k_hi] = hi[:, j, q, :]
                                 codes[rows, 256 * j + k_hi + 4] = lo[:, j, q, :]
-    sc = blocks[:, :, 8192:].reshape(T, G, 4, 4, 4, 2)        # q, b, v, 2 bytes
+    sc = blocks[:, :, 8192:].reshape(T, G, nsc, 4, 4, 4, 2)   # set, q, b, v, 2 bytes
     sv = sc[..., 0].astype(np.uint16) | (sc[..., 1].astype(np.uint16) << 8)
-    for q in range(4):
-        for b in range(4):
-            for v in range(4):
-                scales[np.arange(T) * 64 + 16 * b + 4 * q + v, :] = sv[:, :, q, b, v]
-    return codes, scales
+    for st in range(nsc):
+        for q in range(4):
+            for b in range(4):
+                for v in range(4):
+                    scales[np.arange(T) * 64 + 16 * b + 4 * q + v, st::nsc] = sv[:, :, st, q, b, v]
+    return codes, scales[:, : K // g]
 
 
-@pytest.mark.parametrize("N,K", [(64, 256), (200, 512), (1024, 5120)])
-def test_pack_w4a8_layout(cr, N, K):
+@pytest.mark.parametrize("N,K,g", [(64, 256, 256), (200, 512, 256), (1024, 5120, 256), (64, 384, 128),
+                                   (200, 2688, 128), (72, 1024, 128)])
+def test_pack_w4a8_layout(cr, N, K, g):
     """The packed buffer holds exactly the prepared codes and scales, in the documented order,
-    with zero rows past N."""
+    with zero rows past N (and, for group 128 with K % 256 == 128, zero channels and scales in the
+    last block's upper half)."""
     w = workloads.gaussian_weights(N, K, cfg=96).to(DEV)
-    wq, ws = cr.prepare_weight(w, 256, 4)
-    wp = cr.pack_weight_w4a8(wq, ws)
+    wq, ws = cr.prepare_weight(w, g, 4)
+    wp = cr.pack_weight_w4a8(wq, ws, g)
     torch.cuda.synchronize()
-    assert wp.numel() == cr.packed_bytes_w4a8(N, K)
-    codes, scales = _unpack_w4a8_layout(_np(wp), N, K)
-    assert np.array_equal(codes[:N], orc.unpack_i4(_np(wq)))
-    assert not codes[N:].any() and not scales[N:].any()
+    assert wp.numel() == cr.packed_bytes_w4a8(N, K, g)
+    codes, scales = _unpack_w4a8_layout(_np(wp), N, K, g)
+    assert np.array_equal(codes[:N, :K], orc.unpack_i4(_np(wq)))
+    assert not codes[:, K:].any() and not codes[N:].any() and not scales[N:].any()
     assert np.array_equal(scales[:N], _np(ws).view(np.uint16).T)
+    if g == 128 and K % 256:
+        last = _np(wp)[: -(-N // 64) * -(-K // 256) * 8448].reshape(-1, -(-K // 256), 8448)[:, -1]
+        assert not last[:, 8192 + 128:].any()             # the empty half's scale set
 
 
 def test_linear_w4a8_repeat_and_limits(cr):
