@@ -259,12 +259,12 @@ def bench_decode(cr, wl, torch, steps, warmup):
 
         def gemv4(i):
             cr._call("convrot_linear_w4a8", None, 0, xq.data_ptr(), xsc.data_ptr(), M, N, K, 256,
-                     w4s[i % nw4].data_ptr(), None, y.data_ptr(), None, 0,
+                     w4s[i % nw4].data_ptr(), wp40.numel(), None, y.data_ptr(), None, 0,
                      torch.cuda.current_stream(dev).cuda_stream)
 
         def e2e4(i):
             cr._call("convrot_linear_w4a8", xd.data_ptr(), cr.CONVROT_DTYPE_BF16, None, None, M, N, K, 256,
-                     w4s[i % nw4].data_ptr(), None, y.data_ptr(), ws4.data_ptr(), wsz4,
+                     w4s[i % nw4].data_ptr(), wp40.numel(), None, y.data_ptr(), ws4.data_ptr(), wsz4,
                      torch.cuda.current_stream(dev).cuda_stream)
 
         n4 = max(nw4, 20)
@@ -310,17 +310,56 @@ def bench_w4a4(cr, wl, torch, steps, warmup):
     tp4 = timed(lambda: cr.linear_w4a4_packed(xd, wp4, ws4, bd, out=y))
     t8 = timed(lambda: cr.linear(xd, wq8, ws8, bd, out=y))
     ops = 2.0 * M * N * K
-    promoted = len(wl.mixed_profile_layers())
-    # serving keeps the weights pre-encoded, so the mixed profile uses the packed W4A4 path
-    mixed_ms = (240 - promoted) * tp4 + promoted * t8
+    del wq4, wq8, ws8, wp4, xq4, xs4
+    torch.cuda.empty_cache()
+    mixed = bench_mixed(cr, wl, torch, M, K, N, bd)
+    # cross-check: the same counts of separately timed single-shape linears (serving keeps the
+    # W4A4 weights pre-encoded, so the packed path)
+    promoted = mixed["w8a8_layers"]
+    mixed["sum_of_single_linears_ms"] = (mixed["layers"] - promoted) * tp4 + promoted * t8
     return dict(M=M, K=K, N=N, gemm_us=tc * 1e3, gemm_tops=ops / (tc * 1e-3) / 1e12,
                 gemm_frac_int8_peak=ops / (tc * 1e-3) / 1e12 / PEAK_INT8_TOPS,
                 gemm_frac_fp6_peak=ops / (tc * 1e-3) / 1e12 / PEAK_FP6_TFLOPS,
                 e2e_us=t4 * 1e3, e2e_tops=ops / (t4 * 1e-3) / 1e12,
                 packed_gemm_us=tpc * 1e3, packed_e2e_us=tp4 * 1e3, packed_e2e_tops=ops / (tp4 * 1e-3) / 1e12,
-                w8a8_e2e_us=t8 * 1e3,
-                mixed_profile=dict(layers=240, w8a8_layers=promoted, total_ms=mixed_ms,
-                                   effective_tops=240 * ops / (mixed_ms * 1e-3) / 1e12))
+                w8a8_e2e_us=t8 * 1e3, mixed_profile=mixed)
+
+
+def bench_mixed(cr, wl, torch, M, K, N, bias, passes: int = 3):
+    """The mixed profile as one timed schedule: MIXED_COUNT linears of the W4A4 shape in instance
+    order, the seeded MIXED_PROMOTED of them W8A8 and the rest W4A4 on pre-encoded weights, every
+    instance with its own resident weight (drawn on the device), each a full linear from bf16
+    activations (a ring of 8 inputs).  Pass 0 warms up; the median of the timed passes is
+    reported."""
+    from int4_quantized_linear_amd.mixed import MixedSchedule
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    count = wl.MIXED_COUNT
+    promoted = wl.mixed_profile_layers(count, wl.MIXED_PROMOTED)
+    t0 = time.perf_counter()
+    sched = MixedSchedule(M, K, N, count, promoted, lambda i: wl.mixed_weight(i, N, K, dev), bias=bias)
+    torch.cuda.synchronize()
+    log("mixed: %d instances (%d W8A8) prepared in %.1f s, %.1f GB of weights resident" % (
+        count, len(promoted), time.perf_counter() - t0, sched.weight_bytes() / 1e9))
+    xs = [wl.mixed_acts(j, M, K, dev) for j in range(8)]
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    per = []
+    for rep in range(passes):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        sched.run(xs, ys)
+        e1.record(st)
+        e1.synchronize()
+        if rep:
+            per.append(e0.elapsed_time(e1))
+    total = statistics.median(per)
+    ops = 2.0 * M * N * K
+    log("mixed: %d linears in %.2f ms (%.0f TOP/s)" % (count, total, count * ops / (total * 1e-3) / 1e12))
+    del sched, xs, ys
+    torch.cuda.empty_cache()
+    return dict(layers=count, w8a8_layers=int(len(promoted)), total_ms=total,
+                effective_tops=count * ops / (total * 1e-3) / 1e12,
+                timing="one timed run of the whole schedule (median of %d passes after a warm-up pass)" % (passes - 1))
 
 
 def bench_stack(cr, wl, torch, layers: int):

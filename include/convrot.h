@@ -82,7 +82,10 @@ int convrot_prepare_weight(const void *w, int w_dtype, int64_t N, int64_t K, int
 
 /*
  * Online activation quantization: rotate each token row by the same R and quantize it
- * dynamically (one scale per token for INT8, per (token, group) for INT4).  Same layouts as
+ * dynamically (one scale per token for INT8, per (token, group) for INT4).  The activations get
+ * the same grouped rotation as the weights (nvfp4-convrot page, section 五: the W4A4 variant
+ * rotates activations and weights; on the INT8 path of section 四 the rotation cancels in the
+ * product only if both operands carry it), and RTN as in section 五's --simple mode.  Same layouts as
  * convrot_prepare_weight with M rows.  Exposed so one quantized input can feed several linears
  * (for example q/k/v or gate/up projections that share an input).
  */
@@ -176,7 +179,10 @@ int convrot_linear_w4a4_packed(const void *x, int x_dtype, const uint8_t *xq, co
  *   x bf16/fp32 [M, K] rotated and quantized to INT8 into the workspace, or x = NULL and the
  *   caller's xq int8 [M, K] / x_scale fp32 [M] from convrot_quantize_act(bits = 8).
  *   w_packed: the weights in the W4A8 block layout, from convrot_pack_weight_w4a8 (group 256) or
- *   convrot_pack_weight_w4a8_group with this same group.
+ *   convrot_pack_weight_w4a8_group with this same group; w_packed_bytes must be exactly
+ *   convrot_packed_bytes_w4a8_group(N, K, group).  The two groups' layouts differ in size for every
+ *   shape, so weights packed with the other group are rejected (CONVROT_ERR_SHAPE) rather than
+ *   read past their end or misread.
  *   group 256, or 128 for a width 256 does not divide (nvfp4-convrot page, section 四, detail 3,
  *   dynamic group); K % group == 0, N % 8 == 0, 0 <= M <= CONVROT_W4A8_MAX_M
  *   (CONVROT_ERR_SHAPE otherwise; larger batches belong on convrot_linear or convrot_linear_w4a4).
@@ -185,8 +191,8 @@ int convrot_linear_w4a4_packed(const void *x, int x_dtype, const uint8_t *xq, co
  *   x = NULL none is needed (may be NULL).
  */
 int convrot_linear_w4a8(const void *x, int x_dtype, const int8_t *xq, const float *x_scale, int64_t M, int64_t N,
-                        int64_t K, int group, const void *w_packed, const float *bias, void *y, void *workspace,
-                        size_t workspace_bytes, hipStream_t stream);
+                        int64_t K, int group, const void *w_packed, size_t w_packed_bytes, const float *bias, void *y,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Offline re-layout of INT4 weights for convrot_linear_w4a8: wq uint8 [N, K/2] and w_scale fp16
@@ -240,7 +246,7 @@ int convrot_gemm_i4_i32(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t
  * <= max_group dividing K (256 for K = 5120 or 5376, 128 for the K = 2688 adaln projection), or
  * 0 when K <= 0 or max_group is not a power of two in [1, 256].  Pass the result as `group` to
  * convrot_prepare_weight, convrot_quantize_act, convrot_linear and, for 128 or 256,
- * convrot_linear_w4a4 (the W4A8 decode path needs 256).
+ * convrot_linear_w4a4 and convrot_linear_w4a8 (the W4A4 and W4A8 paths take 256 or 128).
  */
 int convrot_dynamic_group(int64_t K, int max_group);
 

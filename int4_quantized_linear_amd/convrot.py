@@ -31,7 +31,7 @@ SIGNATURES = {
     "convrot_pack_weight_w4a4": ([P, I64, I64, P, P], I),
     "convrot_packed_bytes_w4a4": ([I64, I64], SZ),
     "convrot_linear_w4a4_packed": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, P, SZ, P], I),
-    "convrot_linear_w4a8": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, SZ, P], I),
+    "convrot_linear_w4a8": ([P, I, P, P, I64, I64, I64, I, P, SZ, P, P, P, SZ, P], I),
     "convrot_pack_weight_w4a8": ([P, P, I64, I64, P, P], I),
     "convrot_packed_bytes_w4a8": ([I64, I64], SZ),
     "convrot_pack_weight_w4a8_group": ([P, P, I64, I64, I, P, P], I),
@@ -249,8 +249,10 @@ def linear_w4a8(x: torch.Tensor | None, w_packed: torch.Tensor, N: int, bias: to
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     # the workspace only holds the quantized tokens when x is given
     ws = None if x is None else torch.empty(max(workspace_bytes_w4a8(M, N, K), 256), dtype=torch.uint8, device=dev)
+    # the library checks the packed size against this group's layout (the two groups' sizes differ)
     _call("convrot_linear_w4a8", _ptr(x), _dtype_code(x) if x is not None else 0, _ptr(xq), _ptr(x_scale), M, N, K,
-          group, _ptr(w_packed), _ptr(bias), _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+          group, _ptr(w_packed), w_packed.numel() * w_packed.element_size(), _ptr(bias), _ptr(y), _ptr(ws),
+          0 if ws is None else ws.numel(), _stream(dev))
     return y
 
 

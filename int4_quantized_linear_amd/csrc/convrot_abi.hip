@@ -410,8 +410,8 @@ int convrot_pack_weight_w4a8_group(const uint8_t *wq, const uint16_t *w_scale, i
 }
 
 int convrot_linear_w4a8(const void *x, int x_dtype, const int8_t *xq, const float *x_scale, int64_t M, int64_t N,
-                        int64_t K, int group, const void *w_packed, const float *bias, void *y, void *workspace,
-                        size_t workspace_bytes, hipStream_t stream)
+                        int64_t K, int group, const void *w_packed, size_t w_packed_bytes, const float *bias, void *y,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     const char *who = "convrot_linear_w4a8";
     int rc = check_shape(M, N, K, group, who);
@@ -425,6 +425,13 @@ int convrot_linear_w4a8(const void *x, int x_dtype, const int8_t *xq, const floa
     if (N % 8) return fail(CONVROT_ERR_SHAPE, "%s: N=%lld must be a multiple of 8", who, (long long)N);
     if (M == 0 || N == 0) return CONVROT_OK;
     if (!w_packed || !y) return fail(CONVROT_ERR_NULL, "%s: w_packed and y must be non-NULL", who);
+    // the packed size depends on the group (8320 or 8448 bytes per 64 x 256 block): a buffer packed
+    // with the other group has another size, and would be read past its end or misread
+    const size_t need = convrot_packed_bytes_w4a8_group(N, K, group);
+    if (w_packed_bytes != need)
+        return fail(CONVROT_ERR_SHAPE, "%s: w_packed_bytes=%zu, but weights packed for N=%lld K=%lld group=%d take %zu "
+                    "bytes (were they packed with the other group?)", who, w_packed_bytes, (long long)N, (long long)K,
+                    group, need);
     if (!x && (!xq || !x_scale)) return fail(CONVROT_ERR_NULL, "%s: give x, or both xq and x_scale", who);
     if (x && x_dtype != CONVROT_DTYPE_F32 && x_dtype != CONVROT_DTYPE_BF16)
         return fail(CONVROT_ERR_DTYPE, "%s: x_dtype=%d", who, x_dtype);

@@ -90,6 +90,20 @@ __device__ __forceinline__ void swap32f(float &a, float &b)
 // bits of the returned float's bit pattern (valid for |x*m| < 2^22).
 __device__ __forceinline__ uint32_t rne_bits(float x, float m) { return __float_as_uint(__builtin_fmaf(x, m, kMagicRound)); }
 
+// fp16 nearest-even rounding of the exact quotient a / d (a >= 0, d > 0, both fp32) with a single
+// rounding.  Rounding the fp32 quotient to fp16 would round twice; instead the fp32 quotient is
+// first made round-to-odd (the correctly rounded q, moved one ulp towards the true value when it
+// is inexact and its last bit is even; the remainder a - q*d is exact in one fma and gives the
+// direction), and round-to-odd at 24 bits followed by nearest-even at 11 bits is exact rounding.
+__device__ __forceinline__ __half f16_quotient_rne(float a, float d)
+{
+    const float q = a / d;
+    const float r = __builtin_fmaf(-q, d, a);
+    uint32_t b = __float_as_uint(q);
+    if (r != 0.0f && !(b & 1u)) b += r > 0.0f ? 1u : (b ? 0xffffffffu : 0u);
+    return __float2half_rn(__uint_as_float(b));
+}
+
 // Low bytes of four rne_bits() results -> one packed dword (byte 0 = t0).
 __device__ __forceinline__ uint32_t pack4_i8(uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3)
 {

@@ -66,7 +66,7 @@ struct GemmParams {
     const float *sw;
     const float *bias;
     void *y;
-    int64_t M, N;
+    int M, N;                  // < 2^31 (checked by the C-ABI layer)
     int K;
     int tiles_m, tiles_n;
     // Split-K tail: the first T_dp tiles of the tile order are computed whole; each of the r =
@@ -80,6 +80,17 @@ struct GemmParams {
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// Buffer descriptor from a wave-uniform address and size, built from readfirstlane'd halves so it
+// stays in scalar registers.  (readfirstlane returns int: each half goes through uint32_t, so the
+// low half is zero-extended, not sign-extended, into the 64-bit address.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(uint64_t a, int bytes)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(((uint64_t)hi << 32) | (uint64_t)lo), (short)0,
+                                             __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
 
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n only.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
@@ -147,12 +158,6 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
         tile_coords(q, p.tiles_m, p.tiles_n, J.tm, J.tn);
         return J;
     };
-    int total = 0;                            // K-tiles in this workgroup's stream
-    for (int j = 0; j < njobs; ++j) {
-        const Job J = job(j);
-        total += J.ke - J.kb;
-    }
-
     // Per-lane load geometry (independent of the tile): instruction i (0..3) of wave w fills
     // LDS rows 8*(8i+w) .. +7 of an operand stage; lane -> row +lane/8 at 16-byte position
     // lane%8, which holds K chunk (lane%8) ^ swz(row).
@@ -164,15 +169,19 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
     }
 
     // Current load-side tile (the stream runs ahead of the compute-side tile).
+    // The tile's operand bases are kept as integers and made into buffer descriptors at each
+    // use from readfirstlane'd halves: they are uniform, and a descriptor value carried through
+    // the loop's job switch could otherwise be placed in VGPRs, which turns every load into a
+    // waterfall loop.
     int ld_tm = 0, ld_tn = 0;
-    __amdgpu_buffer_rsrc_t rw, rx;
+    uint64_t wbase_addr = 0, xbase_addr = 0;
     uint32_t offw[4], offx[4];
     auto set_load_tile = [&](int tm, int tn) {
         ld_tm = tm;
         ld_tn = tn;
         const int64_t m0 = (int64_t)ld_tm * BM, n0 = (int64_t)ld_tn * BN;
-        rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(p.wq + n0 * K), (short)0, NUM_RECORDS, 0x00020000);
-        rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(p.xq + m0 * K), (short)0, NUM_RECORDS, 0x00020000);
+        wbase_addr = reinterpret_cast<uint64_t>(p.wq + n0 * K);
+        xbase_addr = reinterpret_cast<uint64_t>(p.xq + m0 * K);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t o = (uint32_t)(lrow[i] * K + 16 * lchunk[i]);
@@ -186,59 +195,66 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
     auto issue_scales = [&](int t) {
         if constexpr (E == Epi::Bf16) {
             const int64_t m0 = (int64_t)ld_tm * BM, n0 = (int64_t)ld_tn * BN;
-            const int64_t nrem = p.N - n0, mrem = p.M - m0;
-            const __amdgpu_buffer_rsrc_t rs[3] = {
-                __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p.sw + n0), (short)0, (int)(4 * (nrem < BN ? nrem : BN)), 0x00020000),
-                __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p.bias ? p.bias + n0 : p.sw), (short)0,
-                                                  p.bias ? (int)(4 * (nrem < BN ? nrem : BN)) : 0, 0x00020000),
-                __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p.sx + m0), (short)0, (int)(4 * (mrem < BM ? mrem : BM)), 0x00020000)};
+            const int nb = (int)(4 * (p.N - n0 < BN ? p.N - n0 : BN)), mb = (int)(4 * (p.M - m0 < BM ? p.M - m0 : BM));
             uint8_t *sb = smem + SCALE_OFF + (t & (NSCALE - 1)) * SCALE_BYTES;
             if (w < 6) {
+                // array arr = w / 2 (0 sw, 1 bias, 2 sx), picked with wave-uniform scalars so the
+                // descriptor stays in SGPRs
+                const int arr = w >> 1;
+                const float *src = arr == 0 ? p.sw + n0 : arr == 1 ? (p.bias ? p.bias + n0 : p.sw) : p.sx + m0;
+                const int bytes = arr == 0 ? nb : arr == 1 ? (p.bias ? nb : 0) : mb;
+                const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(reinterpret_cast<uint64_t>(src), bytes);
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const int a = 2 * w + j, arr = a >> 2, part = a & 3;
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[arr], (lds_void *)(sb + arr * 1024 + part * 256), 4,
+                    const int part = (2 * w + j) & 3;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(sb + arr * 1024 + part * 256), 4,
                                                              (uint32_t)(part * 256 + 4 * lane), 0, 0, 0);
                 }
             }
         }
     };
-    // Issue the loads of the next K-tile of the stream (8 buffer_load ... lds per wave, plus the
-    // scales with a tile's first K-tile) into LDS stage (g & 1).  The load side walks the stream
-    // in order: K-tile ld_kt of job ld_j is the one it issues next.
-    // The K position goes in the scalar offset, so a K-tile costs no VALU: an out-of-range row's
-    // lane offset (OOB) stays past num_records with any K added.  Only a half K-tile at the end
-    // of K (K % 128 == 64) needs per-lane offsets, to read zeros for the chunks past K.
+    // Load side of the stream.  K-tile ld_kt of job ld_j is the next one it issues, from the
+    // descriptors set by set_load_tile.  issue_ktile() is straight-line code (8 buffer_load ... lds
+    // per wave into LDS stage g & 1, no branch), so the scheduler can spread the loads between
+    // MFMAs; the K position goes in the scalar offset, so a K-tile costs no VALU beyond two selects
+    // per load: chunks past K of a half K-tile at the end of K (K % 128 == 64) and every load once
+    // the stream is exhausted get an out-of-range offset (zeros land in LDS, no memory access).
+    // next_job() moves the load side to the next job when a job's K-tiles have all been issued;
+    // it runs once per job, outside the MFMA-interleaved region, and issues the job's scales then.
     int ld_j = -1, ld_kt = 0, ld_ke = 0;
+    uint32_t ld_done = 0u;                    // OOB once every K-tile of the stream has been issued
     const bool khalf = (K % BK) != 0;
-    auto issue = [&](int g) {
-        if (ld_kt == ld_ke) {
-            const Job J = job(++ld_j);
+    uint32_t tmask[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tmask[i] = lchunk[i] >= (BK / 2) / 16 ? OOB : 0u;   // chunks 4..7: past K
+    // (The load-side counters are uniform; readfirstlane states it, so that they and the branch
+    // on them stay scalar.)
+    auto next_job = [&]() __attribute__((always_inline)) {
+        ld_j = __builtin_amdgcn_readfirstlane(ld_j + 1);
+        // (assigned outside the branch: two branches that each store one counter get merged into
+        // one store through a pointer select, which keeps the counters in scratch memory)
+        ld_done = ld_j < njobs ? 0u : OOB;
+        if (ld_j < njobs) {
+            const Job J = job(ld_j);
             set_load_tile(J.tm, J.tn);
             issue_scales(ld_j);
-            ld_kt = J.kb;
-            ld_ke = J.ke;
+            ld_kt = __builtin_amdgcn_readfirstlane(J.kb);
+            ld_ke = __builtin_amdgcn_readfirstlane(J.ke);
         }
+    };
+    auto issue_ktile = [&](int g) __attribute__((always_inline)) {
         const int k0 = __builtin_amdgcn_readfirstlane(ld_kt * BK);
-        const bool tail = khalf && ld_kt == KT - 1;
-        ++ld_kt;
+        const uint32_t tsel = (khalf && ld_kt == KT - 1) ? 0xffffffffu : 0u;
         uint8_t *base = smem + (g & (NST - 1)) * STAGE + w * 1024;
-        if (!tail) {
+        const __amdgpu_buffer_rsrc_t rw = uniform_rsrc(wbase_addr, NUM_RECORDS), rx = uniform_rsrc(xbase_addr, NUM_RECORDS);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + 8 * i * 1024), 16, offw[i], k0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(base + OPB + 8 * i * 1024), 16, offx[i], k0, 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool kin = lchunk[i] < (BK / 2) / 16;              // chunks 0..3 exist
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + 8 * i * 1024), 16,
-                                                         kin ? offw[i] : OOB, k0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(base + OPB + 8 * i * 1024), 16,
-                                                         kin ? offx[i] : OOB, k0, 0, 0);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t extra = (tmask[i] & tsel) | ld_done;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + 8 * i * 1024), 16, offw[i] | extra, k0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(base + OPB + 8 * i * 1024), 16, offx[i] | extra, k0,
+                                                     0, 0);
         }
+        ld_kt = __builtin_amdgcn_readfirstlane(ld_kt + 1);
     };
 
     // Fragment addressing: row = wave base + 32*blk + lane%32 (bases are multiples of 32, so
@@ -278,7 +294,7 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
     // and so drain every store and prefetch in flight.
     auto epilogue = [&](const Job &J, int j) {
         const int m0 = J.tm * BM, n0 = J.tn * BN;
-        const int Mi = (int)p.M, Ni = (int)p.N;
+        const int Mi = p.M, Ni = p.N;
         // lane-dependent bases laundered so the addresses below are formed here, not hoisted out
         // of the tile loop (where they would stay live through the main loop)
         int erow = frow, ecol = wn * 128 + 4 * fhalf;
@@ -396,55 +412,88 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
     // Stores each wavefront has in flight after an epilogue (vmcnt counts them too; a split
     // unit's partial epilogue issues 32, so the wait after it is a little stricter than needed).
     constexpr int EPI_STORES = E == Epi::Int32 ? 32 : 16;
-    // prologue: K-tile 0 (and tile 0's scales) visible, K-tile 1 in flight, first fragments
-    issue(0);
+    // Instruction interleaving inside one sub-step's scheduling region (sched_group_barrier masks:
+    // 0x008 MFMA, 0x100 LDS read, 0x020 global read): the matrix pipe keeps its queue while the
+    // fragment reads and the global loads go out between its instructions.
+    auto interleave_reads = [] {
+#pragma unroll
+        for (int q = 0; q < 6; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    };
+    // prologue: K-tile 0 (and job 0's scales) visible, K-tile 1 in flight, first fragments
+    next_job();
+    issue_ktile(0);
+    if (ld_kt == ld_ke) next_job();
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    if (total > 1) issue(1);
+    issue_ktile(1);
+    if (ld_kt == ld_ke) next_job();
     read_frags(0, 0, 0);
 
     int g = 0;
     for (int j = 0; j < njobs; ++j) {
-        const Job J = job(j);
-        for (int kt = J.kb; kt < J.ke; ++kt, ++g) {
+        // only the K-tile count of the job stays live through its K loop; the epilogue recomputes
+        // the rest (scalar registers are scarce here)
+        int nkt, first = 1;
+        {
+            const Job J = job(j);
+            nkt = __builtin_amdgcn_readfirstlane(J.ke - J.kb);
+        }
+        for (int kt = 0; kt < nkt; ++kt, ++g, first = 0) {
+            // sub-steps 0..2: MFMAs on the fragments read one sub-step earlier, the next
+            // sub-step's fragments read between them
             read_frags(g, 1, 1);
-            fence();
             mfmas(0);
+            interleave_reads();
             fence();
             read_frags(g, 2, 0);
-            fence();
             mfmas(1);
+            interleave_reads();
             fence();
             read_frags(g, 3, 1);
-            fence();
             mfmas(0);
+            interleave_reads();
             fence();
-            // K-tile g+1 must have landed before its first fragments are read.  Issued after
-            // its loads: at most the previous tile's epilogue stores, right after an epilogue
-            // (and only with 16-byte stores; otherwise wait for everything).
-            if (g + 1 < total) {
-                if (VEC && j > 0 && kt == J.kb) __builtin_amdgcn_s_waitcnt(waitcnt_vm(EPI_STORES));
-                else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-            }
+            // sub-step 3 starts before the barrier: these MFMAs use registers only, and keep the
+            // matrix pipe busy while the wavefronts meet
+            mfma_range(1, 0, 2);
+            fence();
+            // K-tile g+1 must have landed before its first fragments are read: at most the
+            // previous tile's epilogue stores may still be in flight right after an epilogue (and
+            // only with 16-byte stores; otherwise wait for everything).
+            if (VEC && j > 0 && first) __builtin_amdgcn_s_waitcnt(waitcnt_vm(EPI_STORES));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             // Every wave has completed (lgkmcnt(0)) its reads of stage g & 1 and waited for its
             // loads of K-tile g+1.  A raw barrier: the fence of __syncthreads() would make the
             // compiler wait for every store in flight as well.
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            // last sub-step: the loads of K-tile g+2 and the first fragments of g+1 are issued
-            // between its MFMAs, so the matrix pipe is fed while they go out
-            mfma_range(1, 0, 2);
+            // rest of sub-step 3: the loads of K-tile g+2 into the stage just freed and the first
+            // fragments of K-tile g+1 go out between the MFMAs (past the end of the stream the
+            // loads are out of range and the reads of a stale stage are never used)
+            issue_ktile(g);
+            read_frags(g + 1, 0, 0);
+            mfma_range(1, 2, 8);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             fence();
-            if (g + 2 < total) issue(g + 2);
-            fence();
-            mfma_range(1, 2, 4);
-            fence();
-            if (g + 1 < total) read_frags(g + 1, 0, 0);
-            fence();
-            mfma_range(1, 4, 8);
+            if (ld_kt == ld_ke) next_job();
             fence();
         }
-        epilogue(J, j);
+        epilogue(job(j), j);
     }
+    // the stream's last (out-of-range) loads write zeros into LDS: let them land before the
+    // workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
 // Split-K tail, second pass: for each split tile, sum its S int32 partial slots (exact, in any
@@ -588,8 +637,8 @@ hipError_t launch_gemm_i8(const int8_t *xq, const int8_t *wq, const float *sx, c
     p.sw = sw;
     p.bias = bias;
     p.y = y;
-    p.M = M;
-    p.N = N;
+    p.M = (int)M;
+    p.N = (int)N;
     p.K = K;
     // the tile walk counts tiles in int
     if (((M + BM - 1) / BM) * ((N + BN - 1) / BN) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;

@@ -85,13 +85,19 @@ __global__ void __launch_bounds__(256) pack_w4a8_kernel(const uint8_t *__restric
             const uint8_t *src = wq + row * Kh + (int64_t)j * (GS / 2);
             for (int h = 0; h < 2; ++h) {                // K-step kk = 2i + h
                 const int kk = 2 * i + h;
+                // K % 128 == 0, so a 64-channel K-step lies wholly below K or wholly past it (the
+                // zero upper half of the last block when K % 256 == 128): one test per K-step
+                // keeps the byte loads below unconditional
+                if (j * GS + 64 * kk >= K) continue;
                 uint32_t nib[16];
+#pragma unroll
                 for (int s = 0; s < 16; ++s) {
                     const int k = 64 * kk + 16 * q + s;  // channel within the block
-                    const uint8_t byte = j * GS + k < K ? src[k >> 1] : (uint8_t)0;   // past K: zero
+                    const uint8_t byte = src[k >> 1];
                     nib[s] = (k & 1) ? (byte >> 4) : (byte & 15u);
                 }
                 uint32_t dA = 0, dB = 0;
+#pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     dA |= ((nib[u] << 4) | nib[4 + u]) << (8 * u);
                     dB |= ((nib[8 + u] << 4) | nib[12 + u]) << (8 * u);

@@ -37,6 +37,7 @@ struct RQParams {
     int rows_per_wg;     // rows handled by one workgroup per iteration (<= 64)
     int ngroups;         // ceil(rows / rows_per_wg)
     float cg;            // 1/sqrt(g) in fp32
+    double root;         // sqrt(g) in fp64
 };
 
 constexpr uint32_t OOB = 0x80000000u;   // buffer offset past num_records: loads read 0, stores drop
@@ -213,6 +214,14 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
             }
         }
 
+        // fp32 of a normalised maximum, from the maximum of the unnormalised sums: for even LG,
+        // 1/sqrt(g) is a power of two and the product is exact; otherwise the division by sqrt(g)
+        // runs in fp64 and is rounded once to fp32, which is the fp32 rounding of the
+        // normalised value whenever the unnormalised fp32 sum is exact
+        auto normalised = [&](float m_u) -> float {
+            if constexpr (LG % 2 == 0) return m_u * p.cg;
+            else return (float)((double)m_u / p.root);
+        };
         // sign left on this lane's values by the lane-exchange butterflies
         const float lsign = (((LG > 3 ? qd : 0) ^ (LG > 4 ? qd >> 1 : 0)) & 1) ? -1.0f : 1.0f;
         float mult[SETS][HS];
@@ -229,7 +238,7 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
 #pragma unroll
             for (int s = 0; s < SETS; ++s) {
                 const float amax = __uint_as_float(smax[par][rr[s] < 64 ? rr[s] : 63]);
-                const float sc = (amax * p.cg) / 127.0f;
+                const float sc = normalised(amax) / 127.0f;
                 mult[s][0] = sc > 0.0f ? lsign * (p.cg / sc) : 0.0f;
                 if (ok[s] && jj[s] == 0 && qd == 0 && h == 0) static_cast<float *>(p.scale)[row0 + rr[s]] = sc;
             }
@@ -240,7 +249,8 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
             for (int s = 0; s < SETS; ++s)
 #pragma unroll
                 for (int hs = 0; hs < HS; ++hs) {
-                    const __half sh = __float2half_rn((m[s][hs] * p.cg) / 7.0f);
+                    // one rounding to fp16 from the exact quotient (no double rounding through fp32)
+                    const __half sh = f16_quotient_rne(normalised(m[s][hs]), 7.0f);
                     const float sc = __half2float(sh);
                     mult[s][hs] = sc > 0.0f ? lsign * (p.cg / sc) : 0.0f;
                     const int64_t grp = (int64_t)jj[s] * HS + hs;
@@ -365,7 +375,8 @@ hipError_t launch_rotate_quant(const void *x, bool x_f32, int64_t rows, int K, i
     p.slots_per_row = (K + 255) / 256;
     p.rows_per_wg = R;
     p.ngroups = (int)((rows + R - 1) / R);
-    p.cg = (float)(1.0 / __builtin_sqrt((double)(1 << log2g)));
+    p.root = __builtin_sqrt((double)(1 << log2g));
+    p.cg = (float)(1.0 / p.root);
     static const int cus = [] {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)

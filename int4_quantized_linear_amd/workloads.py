@@ -162,3 +162,26 @@ def stack_acts(layer: int, key: int, M: int, K: int, device, frac: float = 0.01,
     ch = torch.randperm(K, generator=go, device=device)[: int(round(frac * K))]
     x[:, ch] *= factor
     return x.to(torch.bfloat16)
+
+
+# Mixed W4A4 / W8A8 profile: MIXED_COUNT instances of the W4A4 shape, MIXED_PROMOTED of them
+# (mixed_profile_layers) running W8A8.
+MIXED_COUNT, MIXED_PROMOTED = 240, 48
+
+
+def mixed_weight(inst: int, N: int, K: int, device, std: float = 0.02) -> torch.Tensor:
+    """Weight of one instance of the mixed profile, drawn on the device (240 of them would take
+    minutes on the host): bf16 N(0, std), seeded per instance."""
+    g = _device_generator(CFG_W4A4, 1000 + inst, ROLE_W, device)
+    return (torch.randn(N, K, generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
+
+
+def mixed_acts(key: int, M: int, K: int, device, frac: float = 0.005, factor: float = 50.0) -> torch.Tensor:
+    """Activation of the mixed profile drawn on the device: N(0, 1) with round(frac*K) channels
+    scaled by `factor` (the prefill distribution), bf16, seeded per key."""
+    g = _device_generator(CFG_W4A4, 1000 + key, ROLE_X, device)
+    x = torch.randn(M, K, generator=g, device=device, dtype=torch.float32)
+    go = _device_generator(CFG_W4A4, 1000 + key, ROLE_OUTLIER, device)
+    ch = torch.randperm(K, generator=go, device=device)[: int(round(frac * K))]
+    x[:, ch] *= factor
+    return x.to(torch.bfloat16)

@@ -3,9 +3,12 @@
 (a) quantized codes: |delta| <= 1 LSB everywhere, mismatch rate <= 1e-4 (fp32 rotation sums may
     round differently from the oracle's fp64 sums right at a rounding edge);
 (b) integer accumulators, given identical codes: bit-exact;
-(c) fp32 scales: within 1e-6 relative.  fp16 group scales are themselves values rounded in
-    floating point, so they must be equal except where the fp32 group max differs by rounding:
-    at most 1 fp16 ulp apart, at a mismatch rate <= 1e-3;
+(c) fp32 scales: within 1e-6 relative.  fp16 group scales: both sides round max|group|/7 once
+    to fp16 from an fp32 group maximum, so they are bit-equal unless the two fp32 maxima differ
+    (the rotation sums' rounding order) right at an fp16 rounding edge; such a scale is then
+    1 ulp (2^-10 relative) away, which 1e-6 cannot express, so the rule for fp16 scales is
+    "equal, except at most 1 ulp apart at a mismatch rate <= 1e-4" (measured on 32k-64k scales
+    by the large-sample test);
 (d) bf16 output: max|y_gpu - y_oracle| / max|y_oracle| <= 1e-2, against the oracle's quantized
     result (not the exact product), plus a tighter check that almost every element is within a
     couple of bf16 ulps of it.
@@ -17,7 +20,7 @@ import torch
 
 CODE_MISMATCH_RATE = 1e-4
 SCALE_RTOL = 1e-6
-F16_SCALE_MISMATCH_RATE = 1e-3
+F16_SCALE_MISMATCH_RATE = 1e-4
 Y_REL_TOL = 1e-2
 
 
@@ -62,13 +65,14 @@ def check_scales_f32(gpu: np.ndarray, ref: np.ndarray, what: str = "scales"):
         what, bad.sum(), SCALE_RTOL, (err / np.maximum(np.abs(ref), 1e-300)).max())
 
 
-def check_scales_f16(gpu: np.ndarray, ref: np.ndarray, what: str = "fp16 scales"):
+def check_scales_f16(gpu: np.ndarray, ref: np.ndarray, what: str = "fp16 scales", slack: bool = True):
     g = gpu.astype(np.float16).view(np.uint16).astype(np.int64)
     r = ref.astype(np.float16).view(np.uint16).astype(np.int64)
     d = np.abs(g - r)
     assert d.max(initial=0) <= 1, "%s: scales differ by %d fp16 ulps" % (what, d.max())
     mism = np.count_nonzero(d)
-    assert mism <= max(1, F16_SCALE_MISMATCH_RATE * d.size), "%s: %d of %d differ" % (what, mism, d.size)
+    limit = allowed_mismatches(d.size, F16_SCALE_MISMATCH_RATE) if slack else F16_SCALE_MISMATCH_RATE * d.size
+    assert mism <= limit, "%s: %d of %d differ (limit %.1f)" % (what, mism, d.size, limit)
     return mism
 
 

@@ -186,9 +186,12 @@ def lin_args(x=A, dt=1, xq=None, xs=None, M=32, N=256, K=512, group=256, wq=B, s
     return (x, dt, xq, xs, M, N, K, group, wq, sw, bias, y, ws, wsb, None)
 
 
-def w48_args(x=A, dt=1, xq=None, xs=None, M=12, N=256, K=512, group=256, wp=B, bias=None, y=D, ws=E,
+def w48_args(x=A, dt=1, xq=None, xs=None, M=12, N=256, K=512, group=256, wp=B, wpb=None, bias=None, y=D, ws=E,
              wsb=1 << 30):
-    return (x, dt, xq, xs, M, N, K, group, wp, bias, y, ws, wsb, None)
+    # wpb: the packed weight size the call states; by default the right one for (N, K, group)
+    if wpb is None:
+        wpb = cr.load().convrot_packed_bytes_w4a8_group(N, K, group)
+    return (x, dt, xq, xs, M, N, K, group, wp, wpb, bias, y, ws, wsb, None)
 
 
 def w4_args(x=A, dt=1, xq=None, xs=None, M=32, N=256, K=512, group=256, wq=B, sw=C, bias=None, y=D, ws=E,
@@ -287,6 +290,10 @@ CASES = [
     ("convrot_linear_w4a8", w48_args(ws=None), "CONVROT_ERR_WORKSPACE"),
     ("convrot_linear_w4a8", w48_args(wsb=256), "CONVROT_ERR_WORKSPACE"),
     ("convrot_linear_w4a8", w48_args(ws=E + 64), "CONVROT_ERR_WORKSPACE"),
+    # weights packed with the other scale group (or any other size): rejected, never read
+    ("convrot_linear_w4a8", w48_args(K=512, group=128, wpb=2 * 4 * 8320), "CONVROT_ERR_SHAPE"),
+    ("convrot_linear_w4a8", w48_args(K=512, group=256, wpb=2 * 4 * 8448), "CONVROT_ERR_SHAPE"),
+    ("convrot_linear_w4a8", w48_args(wpb=0), "CONVROT_ERR_SHAPE"),
     ("convrot_pack_weight_w4a8", (A, C, 64, 320, B, None), "CONVROT_ERR_SHAPE"),
     ("convrot_pack_weight_w4a8", (A, C, 64, 100, B, None), "CONVROT_ERR_SHAPE"),
     ("convrot_pack_weight_w4a8", (A, C, -1, 512, B, None), "CONVROT_ERR_SHAPE"),
@@ -332,8 +339,8 @@ def test_empty_inputs_are_noops(lib):
     assert lib.convrot_linear(None, 1, None, None, 0, 256, 512, 256, None, None, None, None, None, 0, None) == 0
     assert lib.convrot_linear(None, 1, None, None, 16, 0, 512, 256, None, None, None, None, None, 0, None) == 0
     assert lib.convrot_linear_w4a4(None, 1, None, None, 0, 256, 512, 256, None, None, None, None, None, 0, None) == 0
-    assert lib.convrot_linear_w4a8(None, 1, None, None, 0, 256, 512, 256, None, None, None, None, 0, None) == 0
-    assert lib.convrot_linear_w4a8(None, 1, None, None, 5, 0, 512, 256, None, None, None, None, 0, None) == 0
+    assert lib.convrot_linear_w4a8(None, 1, None, None, 0, 256, 512, 256, None, 0, None, None, None, 0, None) == 0
+    assert lib.convrot_linear_w4a8(None, 1, None, None, 5, 0, 512, 256, None, 0, None, None, None, 0, None) == 0
     assert lib.convrot_pack_weight_w4a8(None, None, 0, 512, None, None) == 0
     assert lib.convrot_pack_weight_w4a4(None, 0, 512, None, None) == 0
     assert lib.convrot_linear_w4a4_packed(None, 1, None, None, 0, 256, 512, 256, None, None, None, None, None, 0,
