@@ -127,6 +127,28 @@ int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_
                    int64_t K, int group, const int8_t *wq, const float *w_scale, const float *bias, void *y,
                    void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Size of the fixed scratch array convrot_linear_noalloc uses on each GPU (32 MiB). */
+#define CONVROT_NOALLOC_SCRATCH_BYTES 33554432
+
+/*
+ * convrot_linear for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments (without the workspace),
+ * kernels and result bit for bit as convrot_linear.  The scratch the call needs -- the quantized
+ * activations when x is given (M*K + 4*M bytes, each rounded up to 256) and, when it fits, the
+ * GEMM's split-K partial sums -- lives in a fixed array of CONVROT_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends; no call allocates or frees
+ * anything.  The first call on a device looks the array's address up on that device.
+ * With x given, a shape whose quantized activations exceed the array returns
+ * CONVROT_ERR_WORKSPACE before anything is enqueued (use convrot_linear with a workspace).
+ * Every call on one GPU shares that GPU's array, and it keeps the last call's contents (each call
+ * writes what it reads first, so nothing needs clearing): calls that overlap on one GPU -- on
+ * different streams, or from different threads -- race on it and must be serialised by the
+ * caller; calls in order on one stream are safe.
+ */
+int convrot_linear_noalloc(const void *x, int x_dtype, const int8_t *xq, const float *x_scale, int64_t M, int64_t N,
+                           int64_t K, int group, const int8_t *wq, const float *w_scale, const float *bias, void *y,
+                           hipStream_t stream);
+
 /*
  * W4A4 ConvRot linear (nvfp4-convrot page, section 五): both operands rotated, INT4 per
  * (row, group) with fp16 scales, per-group integer dot products scaled and summed in fp32.

@@ -27,6 +27,7 @@ SIGNATURES = {
     "convrot_quantize_act": ([P, I, I64, I64, I, I, P, P, P], I),
     "convrot_workspace_bytes": ([I64, I64, I64, I], SZ),
     "convrot_linear": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, P, SZ, P], I),
+    "convrot_linear_noalloc": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, P], I),
     "convrot_linear_w4a4": ([P, I, P, P, I64, I64, I64, I, P, P, P, P, P, SZ, P], I),
     "convrot_pack_weight_w4a4": ([P, I64, I64, P, P], I),
     "convrot_packed_bytes_w4a4": ([I64, I64], SZ),
@@ -165,6 +166,21 @@ def linear(x: torch.Tensor | None, wq: torch.Tensor, w_scale: torch.Tensor, bias
         raise ValueError("split_k=False needs a pre-quantized (xq, x_scale) pair")
     _call("convrot_linear", _ptr(x), _dtype_code(x) if x is not None else 0, _ptr(xq), _ptr(x_scale), M, N, K, group,
           _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y), _ptr(ws), ws.numel() if ws is not None else 0, _stream(dev))
+    return y
+
+
+def linear_noalloc(x: torch.Tensor | None, wq: torch.Tensor, w_scale: torch.Tensor, bias: torch.Tensor | None = None,
+                   group: int = 256, xq: torch.Tensor | None = None, x_scale: torch.Tensor | None = None,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """linear() through convrot_linear_noalloc: the library's fixed per-GPU scratch instead of a
+    workspace (the output is allocated here unless ``out`` is given)."""
+    _check_dev(x, wq, w_scale, bias, xq, x_scale, out)
+    N, K = wq.shape
+    M = x.shape[0] if x is not None else xq.shape[0]
+    dev = wq.device
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _call("convrot_linear_noalloc", _ptr(x), _dtype_code(x) if x is not None else 0, _ptr(xq), _ptr(x_scale), M, N, K,
+          group, _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y), _stream(dev))
     return y
 
 

@@ -198,11 +198,17 @@ size_t convrot_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits)
     return ws_layout(M, N, K, bits).total;
 }
 
-int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_scale, int64_t M, int64_t N,
-                   int64_t K, int group, const int8_t *wq, const float *w_scale, const float *bias, void *y,
-                   void *workspace, size_t workspace_bytes, hipStream_t stream)
+} // extern "C"
+
+namespace {
+
+// Shared by convrot_linear (caller's workspace) and convrot_linear_noalloc (the library's fixed
+// scratch array).  scratch_fn, when given, is called only after every precondition holds and
+// returns the scratch buffer (or sets the status), so a rejected call touches no device.
+int linear_i8(const char *who, const void *x, int x_dtype, const int8_t *xq, const float *x_scale, int64_t M,
+              int64_t N, int64_t K, int group, const int8_t *wq, const float *w_scale, const float *bias, void *y,
+              void *workspace, size_t workspace_bytes, void *(*scratch_fn)(int *), hipStream_t stream)
 {
-    const char *who = "convrot_linear";
     int rc = check_shape(M, N, K, group, who);
     if (rc) return rc;
     if (M > 16 && (rc = check_gemm_n(N, who))) return rc;
@@ -215,11 +221,18 @@ int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_
         !aligned(w_scale, 4) || !aligned(y, 16) || (bias && !aligned(bias, 4)))
         return fail(CONVROT_ERR_ALIGN, "%s: misaligned pointer", who);
     const WsLayout L = ws_layout(M, N, K, 8);
-    if (x && (!workspace || workspace_bytes < L.part || !aligned(workspace, 256)))
+    if (scratch_fn && x && workspace_bytes < L.part)
+        return fail(CONVROT_ERR_WORKSPACE, "%s: M*K = %lld needs %zu bytes of scratch; the fixed scratch holds %zu "
+                    "(use convrot_linear with a workspace)", who, (long long)(M * K), L.part, workspace_bytes);
+    if (!scratch_fn && x && (!workspace || workspace_bytes < L.part || !aligned(workspace, 256)))
         return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of at least %zu bytes (got %zu)",
                     who, L.part, workspace ? workspace_bytes : (size_t)0);
     if (M == 0 || N == 0) return CONVROT_OK;
     if ((rc = check_device())) return rc;
+    if (scratch_fn) {
+        workspace = scratch_fn(&rc);
+        if (rc) return rc;
+    }
 
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     // room past the quantized x lets an under-filled GEMM split its tail tiles in K
@@ -244,6 +257,61 @@ int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_
                            : convrot::launch_gemm_i8(xq, wq, x_scale, w_scale, bias, y, convrot::Epi::Bf16, M, N,
                                                       (int)K, part, part_bytes, stream);
     return hip_status(e, M <= 16 ? "gemv_i8" : "gemm_i8");
+}
+
+// Scratch of convrot_linear_noalloc: one fixed array per GPU, held until the process ends.  On
+// the host the array's name is only a stand-in for its device address: the address each device
+// holds is looked up once per device (with that device current) and kept in scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[CONVROT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+
+void *scratch_for_current_device(int *rc)
+{
+    static std::mutex mu;
+    static void *scratch_ptr[MAX_DEVICES];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *rc = fail(CONVROT_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+        return nullptr;
+    }
+    if (dev < 0 || dev >= MAX_DEVICES) {
+        *rc = fail(CONVROT_ERR_DEVICE, "device index %d out of range", dev);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(mu);
+    if (!scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            *rc = fail(CONVROT_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+            return nullptr;
+        }
+        scratch_ptr[dev] = ptr;
+    }
+    *rc = CONVROT_OK;
+    return scratch_ptr[dev];
+}
+
+} // namespace
+
+extern "C" {
+
+int convrot_linear(const void *x, int x_dtype, const int8_t *xq, const float *x_scale, int64_t M, int64_t N,
+                   int64_t K, int group, const int8_t *wq, const float *w_scale, const float *bias, void *y,
+                   void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return linear_i8("convrot_linear", x, x_dtype, xq, x_scale, M, N, K, group, wq, w_scale, bias, y, workspace,
+                     workspace_bytes, nullptr, stream);
+}
+
+int convrot_linear_noalloc(const void *x, int x_dtype, const int8_t *xq, const float *x_scale, int64_t M, int64_t N,
+                           int64_t K, int group, const int8_t *wq, const float *w_scale, const float *bias, void *y,
+                           hipStream_t stream)
+{
+    return linear_i8("convrot_linear_noalloc", x, x_dtype, xq, x_scale, M, N, K, group, wq, w_scale, bias, y, nullptr,
+                     CONVROT_NOALLOC_SCRATCH_BYTES, scratch_for_current_device, stream);
 }
 
 int convrot_gemm_i8_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K, int32_t *acc,

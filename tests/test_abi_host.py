@@ -41,6 +41,7 @@ def test_header_declares_the_boundary():
                  "convrot_pack_weight_w4a8_group", "convrot_packed_bytes_w4a8_group",
                  "convrot_workspace_bytes", "convrot_workspace_bytes_w4a8",
                  "convrot_gemm_i8_i32", "convrot_gemm_i4_i32", "convrot_dynamic_group", "convrot_last_error",
+                 "convrot_linear_noalloc",
                  "convrot_status_string"):
         assert name in fns
     assert set(fns) == set(cr.SIGNATURES), "binding signatures and header disagree"
@@ -245,6 +246,10 @@ CASES = [
     # the tiled GEMM's N limit (2^24); the decode GEMV (M <= 16) takes a larger N
     ("convrot_linear", lin_args(N=1 << 24), "CONVROT_ERR_SHAPE"),
     ("convrot_linear", lin_args(M=16, N=1 << 24, wq=None), "CONVROT_ERR_NULL"),
+    # the no-allocation linear: the same checks, and activations too large for its fixed scratch
+    ("convrot_linear_noalloc", lin_args(K=100)[:12] + (None,), "CONVROT_ERR_SHAPE"),
+    ("convrot_linear_noalloc", lin_args(wq=None)[:12] + (None,), "CONVROT_ERR_NULL"),
+    ("convrot_linear_noalloc", lin_args(M=8192, K=8192)[:12] + (None,), "CONVROT_ERR_WORKSPACE"),
     # W4A4 linear
     ("convrot_linear_w4a4", w4_args(group=64), "CONVROT_ERR_GROUP"),
     ("convrot_linear_w4a4", w4_args(K=384), "CONVROT_ERR_SHAPE"),         # group 256 must divide K
