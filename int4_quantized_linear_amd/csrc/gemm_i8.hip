@@ -52,7 +52,10 @@ constexpr int STAGE = 2 * OPB;                // weight rows then token rows
 constexpr int SCALE_OFF = NST * STAGE;        // 128 KiB
 constexpr int SCALE_BYTES = 4 * (2 * BN + BM);
 constexpr int NSCALE = 4;
-constexpr int SMEM = SCALE_OFF + NSCALE * SCALE_BYTES;
+// 1 KiB per wave that a K-tile's loads target when they are not issued for real (the last
+// K-tile of a job, whose stage the epilogue uses first): out-of-range zeros land here
+constexpr int DUMMY_OFF = SCALE_OFF + NSCALE * SCALE_BYTES;
+constexpr int SMEM = DUMMY_OFF + 8 * 1024;
 constexpr int NTHREADS = 512;
 constexpr int GROUP_M = 4;
 constexpr int WG_PER_CU = 1;
@@ -182,11 +185,14 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
         const int64_t m0 = (int64_t)ld_tm * BM, n0 = (int64_t)ld_tn * BN;
         wbase_addr = reinterpret_cast<uint64_t>(p.wq + n0 * K);
         xbase_addr = reinterpret_cast<uint64_t>(p.xq + m0 * K);
+        // rows left in the operands past the tile's first row (32-bit: N, M < 2^31)
+        const int nrem = __builtin_amdgcn_readfirstlane(p.N - ld_tn * BN);
+        const int mrem = __builtin_amdgcn_readfirstlane(p.M - ld_tm * BM);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t o = (uint32_t)(lrow[i] * K + 16 * lchunk[i]);
-            offw[i] = n0 + lrow[i] < p.N ? o : OOB;
-            offx[i] = m0 + lrow[i] < p.M ? o : OOB;
+            offw[i] = lrow[i] < nrem ? o : OOB;
+            offx[i] = lrow[i] < mrem ? o : OOB;
         }
     };
     // The tile's sw, bias and sx (256 floats each) go to LDS scale buffer (t & 3) with the
@@ -242,19 +248,26 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
             ld_ke = __builtin_amdgcn_readfirstlane(J.ke);
         }
     };
-    auto issue_ktile = [&](int g) __attribute__((always_inline)) {
+    // real == false (the last K-tile of a job): the same instructions, but out of range into the
+    // wave's dummy 1 KiB, and the stream does not advance; the epilogue issues the K-tile for real
+    // once it is done with the stage.  (A uniform select rather than a branch keeps one copy of
+    // the MFMA-interleaved region.)
+    auto issue_ktile = [&](int g, bool real) __attribute__((always_inline)) {
         const int k0 = __builtin_amdgcn_readfirstlane(ld_kt * BK);
         const uint32_t tsel = (khalf && ld_kt == KT - 1) ? 0xffffffffu : 0u;
         uint8_t *base = smem + (g & (NST - 1)) * STAGE + w * 1024;
+        uint8_t *dummy = smem + DUMMY_OFF + w * 1024;
+        const uint32_t skip = real ? 0u : OOB;
         const __amdgpu_buffer_rsrc_t rw = uniform_rsrc(wbase_addr, NUM_RECORDS), rx = uniform_rsrc(xbase_addr, NUM_RECORDS);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t extra = (tmask[i] & tsel) | ld_done;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + 8 * i * 1024), 16, offw[i] | extra, k0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(base + OPB + 8 * i * 1024), 16, offx[i] | extra, k0,
-                                                     0, 0);
+            const uint32_t extra = (tmask[i] & tsel) | ld_done | skip;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(real ? base + 8 * i * 1024 : dummy), 16,
+                                                     offw[i] | extra, k0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(real ? base + OPB + 8 * i * 1024 : dummy), 16,
+                                                     offx[i] | extra, k0, 0, 0);
         }
-        ld_kt = __builtin_amdgcn_readfirstlane(ld_kt + 1);
+        ld_kt = __builtin_amdgcn_readfirstlane(ld_kt + (real ? 1 : 0));
     };
 
     // Fragment addressing: row = wave base + 32*blk + lane%32 (bases are multiples of 32, so
@@ -292,7 +305,20 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
     // lane offsets; out-of-range rows/columns get an out-of-bounds offset and are dropped.  This
     // keeps the epilogue's register footprint small: a spill reload here would wait on vmcnt
     // and so drain every store and prefetch in flight.
-    auto epilogue = [&](const Job &J, int j) {
+    // The epilogue of a job runs after its last K-tile g.  It issues the loads of K-tile g + 2 (in
+    // the K loop they go out during the last sub-step; for a job's last K-tile they wait until
+    // here) before any of its stores, so that the first barrier of the next job can leave the
+    // stores in flight.  The bf16 16-byte-store variant first passes each 32-row block through
+    // the wave's own 8 KiB of the LDS stage K-tile g occupied (every wave has read it: barrier of
+    // K-tile g) -- exactly the 8 pieces of 1 KiB this wave's loads of K-tile g + 2 refill, so no
+    // other wave touches them -- and writes whole 128-byte lines: 4 rows x 256 bytes per store
+    // instruction rather than 32 rows x 32 bytes, a quarter of the write transactions.
+    auto issue_after_epilogue_reads = [&](int g) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // LDS reads of the region done
+        issue_ktile(g, true);
+        if (ld_kt == ld_ke) next_job();
+    };
+    auto epilogue = [&](const Job &J, int j, int g) {
         const int m0 = J.tm * BM, n0 = J.tn * BN;
         const int Mi = p.M, Ni = p.N;
         // lane-dependent bases laundered so the addresses below are formed here, not hoisted out
@@ -300,6 +326,7 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
         int erow = frow, ecol = wn * 128 + 4 * fhalf;
         asm volatile("" : "+v"(erow), "+v"(ecol));
         if constexpr (E == Epi::Int32) {
+            issue_after_epilogue_reads(g);
 #pragma unroll
             for (int bj = 0; bj < 2; ++bj) {
                 const int mr = m0 + wm * 64 + 32 * bj;            // first row of the block (uniform)
@@ -330,6 +357,7 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
             // split unit (16-byte-store variant only): its int32 partial sums go to slot J.slot
             // (BM x BN int32, row-major).  Rows past M and column groups past N are not written,
             // and never read.
+            issue_after_epilogue_reads(g);
             int32_t *slot = p.part + (int64_t)J.slot * (BM * BN);
             // own laundered lane bases, so that no address of this branch is shared with (and kept
             // live across) the bf16 branch
@@ -353,7 +381,73 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
                     }
                 fence();
             }
+        } else if constexpr (VEC) {
+            const float *ls = reinterpret_cast<const float *>(smem + SCALE_OFF + (j & (NSCALE - 1)) * SCALE_BYTES);
+            // the wave's region: piece q (0..7) at 1024 w + 8192 (q & 3) (+ OPB for q >= 4); row r
+            // of a 32-row block is piece r / 4 at (r % 4) * 256, its 16-byte chunk c at position
+            // c ^ (r % 16) (the 16 rows a write instruction's half-wave covers hit 16 bank groups)
+            uint8_t *reg = smem + (g & (NST - 1)) * STAGE + w * 1024;
+            // lane-dependent parts, laundered so that they are formed here rather than hoisted
+            // out of the tile loop (where they would stay live, or spill):
+            //   write side: row erow's base in the region and the XOR key of its chunk positions
+            //   read side:  instruction q reads row r = 4q + rrow, chunk rchunk, at position
+            //               rchunk ^ (r % 16) = (rchunk ^ rrow) ^ 4 (q % 4)
+            int wrow = (erow >> 4) * OPB + 8192 * ((erow >> 2) & 3) + (erow & 3) * 256, wkey = fhalf ^ (erow & 15);
+            int rrow = lane >> 4, rchunk = lane & 15, rkey = rchunk ^ (lane >> 4);
+            asm volatile("" : "+v"(wrow), "+v"(wkey), "+v"(rrow), "+v"(rchunk), "+v"(rkey));
+            const int n = n0 + wn * 128 + 8 * rchunk;
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj) {
+                const float sxm = ls[2 * BN + wm * 64 + 32 * bj + erow];
+#pragma unroll
+                for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+                    for (int g2 = 0; g2 < 2; ++g2) {
+                        // column groups g = 2*g2 and 2*g2+1 of block bi: 4 columns each per lane
+                        uint32_t pk[2][2];
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int gg = 2 * g2 + h;
+                            const int nl = ecol + 32 * bi + 8 * gg;
+                            const v4f s4 = *reinterpret_cast<const v4f *>(ls + nl);
+                            const v4f b4 = *reinterpret_cast<const v4f *>(ls + BN + nl);
+                            float yv[4];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                yv[i] = __builtin_fmaf((float)acc[bi][bj][4 * gg + i], sxm * s4[i], b4[i]);
+                            pk[h][0] = pack_bf16x2(yv[0], yv[1]);
+                            pk[h][1] = pack_bf16x2(yv[2], yv[3]);
+                        }
+                        // lane l < 32 now holds columns 8g..8g+7 of group g = 2*g2, lane l+32 those
+                        // of group 2*g2+1 (same row m = l % 32): chunk 4 bi + 2 g2 + l / 32 of row m
+                        swap32(pk[0][0], pk[1][0]);
+                        swap32(pk[0][1], pk[1][1]);
+                        // chunk 4 bi + 2 g2 + fhalf of row erow, at position chunk ^ (erow % 16)
+                        *reinterpret_cast<v4u *>(reg + wrow + 16 * ((4 * bi + 2 * g2) ^ wkey)) =
+                            v4u{pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
+                    }
+                // back in row order: instruction q reads rows 4q .. 4q+3, 16 lanes per row
+                v4u out[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    out[q] = *reinterpret_cast<const v4u *>(reg + (q >> 2) * OPB + 8192 * (q & 3) + rrow * 256 +
+                                                            16 * (rkey ^ (4 * (q & 3))));
+                // the loads of K-tile g + 2 refill the region: after the last block's reads, before
+                // its stores (the first barrier of the next job then waits for all but those 8)
+                if (bj == 1) issue_after_epilogue_reads(g);
+                const int mr = m0 + wm * 64 + 32 * bj;
+                const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+                    static_cast<uint16_t *>(p.y) + (int64_t)mr * p.N, (short)0, NUM_RECORDS, 0x00020000);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int r = 4 * q + rrow;
+                    const uint32_t off = (mr + r < Mi && n < Ni) ? (uint32_t)(r * Ni + n) * 2u : OOB;
+                    __builtin_amdgcn_raw_buffer_store_b128(out[q], ry, off, 0, 0);
+                }
+                fence();
+            }
         } else {
+            issue_after_epilogue_reads(g);
             const float *ls = reinterpret_cast<const float *>(smem + SCALE_OFF + (j & (NSCALE - 1)) * SCALE_BYTES);
 #pragma unroll
             for (int bj = 0; bj < 2; ++bj) {
@@ -366,37 +460,29 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
                 for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
                     for (int g2 = 0; g2 < 2; ++g2) {
-                        // column groups g = 2*g2 and 2*g2+1 of block bi: 4 columns each per lane
                         uint32_t pk[2][2];
 #pragma unroll
                         for (int h = 0; h < 2; ++h) {
-                            const int g = 2 * g2 + h;
-                            const int nl = ecol + 32 * bi + 8 * g;
+                            const int gg = 2 * g2 + h;
+                            const int nl = ecol + 32 * bi + 8 * gg;
                             const v4f s4 = *reinterpret_cast<const v4f *>(ls + nl);
                             const v4f b4 = *reinterpret_cast<const v4f *>(ls + BN + nl);
                             float yv[4];
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
-                                yv[i] = __builtin_fmaf((float)acc[bi][bj][4 * g + i], sxm * s4[i], b4[i]);
+                                yv[i] = __builtin_fmaf((float)acc[bi][bj][4 * gg + i], sxm * s4[i], b4[i]);
                             pk[h][0] = pack_bf16x2(yv[0], yv[1]);
                             pk[h][1] = pack_bf16x2(yv[2], yv[3]);
                         }
-                        // lane l < 32 now gets columns 8g..8g+7 of group g = 2*g2, lane l+32 those
-                        // of group 2*g2+1 (same token row m)
                         swap32(pk[0][0], pk[1][0]);
                         swap32(pk[0][1], pk[1][1]);
                         const int n = n0 + (ecol - 4 * fhalf) + 32 * bi + 8 * (2 * g2 + fhalf);
-                        if constexpr (VEC) {
-                            const uint32_t off = (rok && n < Ni) ? (uint32_t)(erow * Ni + n) * 2u : OOB;
-                            __builtin_amdgcn_raw_buffer_store_b128(v4u{pk[0][0], pk[0][1], pk[1][0], pk[1][1]}, ry, off, 0, 0);
-                        } else {
-                            // rows not 16-byte aligned (N % 8 != 0): element stores, clipped at N
-                            const uint32_t wv[4] = {pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
+                        // rows not 16-byte aligned (N % 8 != 0): element stores, clipped at N
+                        const uint32_t wv[4] = {pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const uint32_t off = (rok && n + e < Ni) ? (uint32_t)(erow * Ni + n + e) * 2u : OOB;
-                                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(wv[e >> 1] >> (16 * (e & 1))), ry, off, 0, 0);
-                            }
+                        for (int e = 0; e < 8; ++e) {
+                            const uint32_t off = (rok && n + e < Ni) ? (uint32_t)(erow * Ni + n + e) * 2u : OOB;
+                            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(wv[e >> 1] >> (16 * (e & 1))), ry, off, 0, 0);
                         }
                     }
                 fence();
@@ -409,9 +495,10 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
     };
 
     if (njobs <= 0) return;
-    // Stores each wavefront has in flight after an epilogue (vmcnt counts them too; a split
-    // unit's partial epilogue issues 32, so the wait after it is a little stricter than needed).
-    constexpr int EPI_STORES = E == Epi::Int32 ? 32 : 16;
+    // Stores each wavefront issues after the loads of the next job's second K-tile, in an
+    // epilogue (vmcnt counts them too; the int32 and split-unit epilogues issue all 32 of theirs
+    // after those loads; the bf16 one 8 of its 16).
+    constexpr int EPI_STORES = E == Epi::Int32 ? 32 : 8;
     // Instruction interleaving inside one sub-step's scheduling region (sched_group_barrier masks:
     // 0x008 MFMA, 0x100 LDS read, 0x020 global read): the matrix pipe keeps its queue while the
     // fragment reads and the global loads go out between its instructions.
@@ -425,11 +512,11 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
     };
     // prologue: K-tile 0 (and job 0's scales) visible, K-tile 1 in flight, first fragments
     next_job();
-    issue_ktile(0);
+    issue_ktile(0, true);
     if (ld_kt == ld_ke) next_job();
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    issue_ktile(1);
+    issue_ktile(1, true);
     if (ld_kt == ld_ke) next_job();
     read_frags(0, 0, 0);
 
@@ -472,8 +559,9 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             // rest of sub-step 3: the loads of K-tile g+2 into the stage just freed and the first
             // fragments of K-tile g+1 go out between the MFMAs (past the end of the stream the
-            // loads are out of range and the reads of a stale stage are never used)
-            issue_ktile(g);
+            // loads are out of range and the reads of a stale stage are never used).  After a
+            // job's last K-tile the epilogue uses the freed stage first and issues the loads itself.
+            issue_ktile(g, kt + 1 < nkt);
             read_frags(g + 1, 0, 0);
             mfma_range(1, 2, 8);
 #pragma unroll
@@ -489,7 +577,7 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
             if (ld_kt == ld_ke) next_job();
             fence();
         }
-        epilogue(job(j), j);
+        epilogue(job(j), j, g - 1);
     }
     // the stream's last (out-of-range) loads write zeros into LDS: let them land before the
     // workgroup's LDS is released
