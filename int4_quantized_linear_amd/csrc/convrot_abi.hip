@@ -194,7 +194,10 @@ int convrot_quantize_act(const void *x, int x_dtype, int64_t M, int64_t K, int g
 
 size_t convrot_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits)
 {
-    if (M < 0 || N < 0 || K <= 0 || (bits != 8 && bits != 4)) return 0;
+    // the shapes the entry points accept (check_shape), which also keeps every size below in range
+    if (M < 0 || N < 0 || M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K < 64 || K > CONVROT_MAX_K ||
+        K % 64 || (bits != 8 && bits != 4))
+        return 0;
     return ws_layout(M, N, K, bits).total;
 }
 
