@@ -17,9 +17,11 @@ The same run also measures, each with its own timed loop:
   * the CPU oracle on a bounded sample of the prefill workload (cpu_baseline).
 Per-kernel durations come from HIP events recorded on the stream the kernels run on.
 
-Counter runs (HBM traffic): `--only copy` runs a plain 256 MiB device copy for calibrating
+Counter runs (L2-miss traffic): `--only copy` runs a plain 256 MiB device copy for calibrating
 FETCH_SIZE / WRITE_SIZE; `--pmc-summary` turns four rocprofv3 counter CSVs into
-profiles/hbm_traffic.json, which this script reads back for the roofline's `traffic`.
+profiles/hbm_traffic.json, which this script reads back for the roofline's `traffic` (bytes the L2
+requests from the memory side; the last-level cache serves part of them, so they bound the HBM
+traffic from above); `--counter-table` prints per-kernel counter means from --pmc CSVs.
 """
 from __future__ import annotations
 
@@ -41,6 +43,11 @@ PEAK_FP6_TFLOPS = 10100.0    # MI355X dense FP6 MFMA, TFLOP/s (published)
 RING_BYTES = 1 << 30
 COPY_PROBE_BYTES = 256 << 20
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+# What `traffic` counts: the L2's requests to the memory side (FETCH_SIZE + WRITE_SIZE), calibrated
+# on a plain copy.  The 256 MB last-level cache sits behind the L2 and serves part of them, so the
+# figure bounds the kernel's HBM traffic from above rather than equalling it.
+TRAFFIC_KIND = ("L2-miss bytes per launch (TCC FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's counts); "
+                "includes what the last-level cache serves: an upper bound on HBM bytes")
 KERNEL_SOURCES = {"gemm_i8": "gemm_i8.hip", "rotate_quant": "rotate_quant.hip", "gemv_i8": "gemv_i8.hip",
                   "gemm_w4a4": "gemm_w4a4.hip"}
 
@@ -58,6 +65,9 @@ def parse():
     ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a4", "stack", "split", "copy"], default="all",
                     help="restrict the measured workloads (profiling runs); 'copy' = the counter calibration copy")
     ap.add_argument("--stack-layers", type=int, default=64)
+    ap.add_argument("--counter-table", nargs="+", metavar="CSV",
+                    help="print a markdown table of per-dispatch mean counters per kernel from rocprofv3 --pmc "
+                         "counter CSVs (one or more passes) and exit")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from rocprofv3 --pmc counter CSVs and exit")
     return ap.parse_args()
@@ -594,6 +604,61 @@ PMC_COMMANDS = [
 ]
 
 
+def _kernel_label(name: str) -> str:
+    n = name
+    for pre in ("void ", "(anonymous namespace)::", "convrot::"):
+        n = n.replace(pre, "")
+    # keep the template arguments, drop the parameter list
+    depth, cut = 0, len(n)
+    for i, ch in enumerate(n):
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0 and i > 0:
+            cut = i
+            break
+    return n[:cut]
+
+
+COUNTER_KERNELS = ("gemm_i8_kernel", "gemm_w4a4_kernel", "rotate_quant_kernel", "tile_fp6_kernel", "gemv_i8_kernel",
+                   "gemv_w4a8_kernel", "split_reduce_kernel")
+
+
+def counter_table(paths):
+    """Per-dispatch means of every counter in the given rocprofv3 --pmc CSVs, per library kernel,
+    as a markdown table (counters as rows).  Derived rows, per dispatch: MFMA-busy fraction =
+    SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs); L2 hit rate =
+    TCC_HIT / (TCC_HIT + TCC_MISS); mean L2 read latency seen by the L1 = TCP_TCC_READ_REQ_LATENCY /
+    TCP_TCC_READ_REQ (cycles)."""
+    acc = {}
+    for path in paths:
+        for name, cname, v in _counter_rows(path):
+            if not any(k in name for k in COUNTER_KERNELS):
+                continue
+            acc.setdefault(_kernel_label(name), {}).setdefault(cname, []).append(v)
+    kernels = sorted(acc)
+    counters = sorted({c for k in kernels for c in acc[k]})
+    mean = {k: {c: statistics.fmean(v) for c, v in acc[k].items()} for k in kernels}
+    print("| counter | " + " | ".join("`%s`" % k for k in kernels) + " |")
+    print("|---|" + "---|" * len(kernels))
+    print("| dispatches | " + " | ".join("%d" % max(len(v) for v in acc[k].values()) for k in kernels) + " |")
+    for c in counters:
+        print("| %s | " % c + " | ".join("%.4g" % mean[k][c] if c in mean[k] else "" for k in kernels) + " |")
+
+    def derived(label, fn):
+        vals = []
+        for k in kernels:
+            try:
+                vals.append(fn(mean[k]))
+            except (KeyError, ZeroDivisionError):
+                vals.append("")
+        if any(v != "" for v in vals):
+            print("| *%s* | " % label + " | ".join(v if isinstance(v, str) else "%.3g" % v for v in vals) + " |")
+
+    derived("MFMA-busy fraction", lambda m: m["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * m["GRBM_GUI_ACTIVE"] / 8))
+    derived("L2 hit rate", lambda m: m["TCC_HIT_sum"] / (m["TCC_HIT_sum"] + m["TCC_MISS_sum"]))
+    derived("mean L2 read latency (cycles)", lambda m: m["TCP_TCC_READ_REQ_LATENCY_sum"] / m["TCP_TCC_READ_REQ_sum"])
+
+
 def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     f = _per_dispatch_kib(fetch_csv, "FETCH_SIZE")
     w = _per_dispatch_kib(write_csv, "WRITE_SIZE")
@@ -626,6 +691,9 @@ def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.counter_table:
+        counter_table(args.counter_table)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path (run with --gpus 1)",
@@ -689,6 +757,7 @@ def main():
                          "achieved": gemm_tops, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                          "frac": gemm_tops / PEAK_INT8_TOPS,
                          "traffic": traffic_from_profiles("gemm_i8_prefill", h),
+                         "traffic_kind": TRAFFIC_KIND,
                          "algorithmic_bytes": p["gemm_bytes"], "source_hash": h},
             "kernels": {"rotate_quant_us": p["rq_ms"] * 1e3, "rotate_quant_GBps": rq_gbs,
                         "rotate_quant_frac_hbm": rq_gbs / PEAK_HBM_GBS,

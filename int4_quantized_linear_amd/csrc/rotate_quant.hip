@@ -49,6 +49,61 @@ __device__ __forceinline__ void bfly(float &a, float &b)
     a = s;
 }
 
+// Unnormalised Walsh-Hadamard transform of one slot held as 4 chunks x 8 values per lane (the
+// register layout above), on channel bits < LG.  qd = lane & 3.
+template <int LG>
+__device__ __forceinline__ void fwht_slot(float (&v)[4][8], int qd)
+{
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int b = 0; b < 3; ++b) {
+            if (LG > b) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (!(e & (1 << b))) bfly(v[r][e], v[r][e | (1 << b)]);
+            }
+        }
+    }
+    // channel bits 6 and 7: chunk registers
+    if constexpr (LG > 6) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { bfly(v[0][e], v[1][e]); bfly(v[2][e], v[3][e]); }
+    }
+    if constexpr (LG > 7) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { bfly(v[0][e], v[2][e]); bfly(v[1][e], v[3][e]); }
+    }
+    // channel bit 5: swap it with chunk bit 0 (channel bit 6) between lane halves, then butterfly
+    // in registers.  Afterwards v[2*r1 + c5][e] holds channel bit 5 = c5 and channel bit 6 =
+    // lane bit 5.
+    if constexpr (LG > 5) {
+#pragma unroll
+        for (int r1 = 0; r1 < 2; ++r1)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                swap32f(v[2 * r1][e], v[2 * r1 + 1][e]);
+                bfly(v[2 * r1][e], v[2 * r1 + 1][e]);
+            }
+    }
+    // channel bits 3 and 4, last: partner is lane ^ 1 / lane ^ 2.  Each stage is one
+    // v_fmac_f32_dpp per value: self + partner * c, c = +1 on the lower lane (a + b, correct) and
+    // -1 on the upper lane (b - a, the negated result).  Running the two lane stages after all
+    // others keeps that sign error out of every other butterfly: the final value of a lane is off
+    // by the sign (-1)^(bit0 ^ bit1) of its quad position, which is folded into the quantization
+    // multiplier and does not change |v|.
+    if constexpr (LG > 3) {
+        const float c = (qd & 1) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) fmac_dpp8_xor1_(v[r], c);
+    }
+    if constexpr (LG > 4) {
+        const float c = (qd & 2) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) fmac_dpp8_xor2_(v[r], c);
+    }
+}
+
 // LG = log2 of the rotation group (0..8), a template parameter so that the butterfly stages are
 // straight-line code.  All global accesses are buffer instructions whose out-of-range lanes get
 // an out-of-bounds offset (loads return 0, stores are dropped): no branches around them, so the
@@ -141,57 +196,7 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
 
         // ---- unnormalised Walsh-Hadamard butterflies on channel bits < LG
 #pragma unroll
-        for (int s = 0; s < SETS; ++s) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-#pragma unroll
-                for (int b = 0; b < 3; ++b) {
-                    if (LG > b) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (!(e & (1 << b))) bfly(v[s][r][e], v[s][r][e | (1 << b)]);
-                    }
-                }
-            }
-            // channel bits 6 and 7: chunk registers
-            if constexpr (LG > 6) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) { bfly(v[s][0][e], v[s][1][e]); bfly(v[s][2][e], v[s][3][e]); }
-            }
-            if constexpr (LG > 7) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) { bfly(v[s][0][e], v[s][2][e]); bfly(v[s][1][e], v[s][3][e]); }
-            }
-            // channel bit 5: swap it with chunk bit 0 (channel bit 6) between lane halves, then
-            // butterfly in registers.  Afterwards v[s][2*r1 + c5][e] holds channel bit 5 = c5 and
-            // channel bit 6 = lane bit 5.
-            if constexpr (LG > 5) {
-#pragma unroll
-                for (int r1 = 0; r1 < 2; ++r1)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        swap32f(v[s][2 * r1][e], v[s][2 * r1 + 1][e]);
-                        bfly(v[s][2 * r1][e], v[s][2 * r1 + 1][e]);
-                    }
-            }
-            // channel bits 3 and 4, last: partner is lane ^ 1 / lane ^ 2.  Each stage is one
-            // v_fmac_f32_dpp per value: self + partner * c, c = +1 on the lower lane (a + b,
-            // correct) and -1 on the upper lane (b - a, the negated result).
-            // Running the two lane stages after all others keeps that sign error out of every
-            // other butterfly: the final value of a lane is off by the sign (-1)^(bit0 ^ bit1)
-            // of its quad position, which is folded into the quantization multiplier below and
-            // does not change |v|.
-            if constexpr (LG > 3) {
-                const float c = (qd & 1) ? -1.0f : 1.0f;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) fmac_dpp8_xor1_(v[s][r], c);
-            }
-            if constexpr (LG > 4) {
-                const float c = (qd & 2) ? -1.0f : 1.0f;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) fmac_dpp8_xor2_(v[s][r], c);
-            }
-        }
+        for (int s = 0; s < SETS; ++s) fwht_slot<LG>(v[s], qd);
 
         // ---- absmax: per slot over its 8 lanes (lane bits 0, 1 and 5); for INT4 with 128-channel
         // groups, per half slot: channel bit 7 is the register pair (registers 0, 1 | 2, 3)

@@ -69,3 +69,21 @@ def test_pmc_summary_calibrates_against_the_copy(tmp_path, monkeypatch, capsys):
     assert g["source_hash"] == bench.src_hash("gemm_i8.hip")
     assert d["kernels"]["rotate_quant_prefill"]["source_hash"] == bench.src_hash("rotate_quant.hip")
     assert "copy" not in d["kernels"]
+
+
+def test_counter_table_means_and_derived_rows(tmp_path, capsys):
+    gemm = "void convrot::(anonymous namespace)::gemm_i8_kernel<(convrot::Epi)0, true>(convrot::(anonymous namespace)::GemmParams)"
+    torch_kernel = "void at::native::vectorized_elementwise_kernel<4>(int)"
+    a, b = str(tmp_path / "a.csv"), str(tmp_path / "b.csv")
+    _counter_csv(a, [(gemm, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 300.0), (gemm, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 500.0),
+                     (gemm, "GRBM_GUI_ACTIVE", 8 * 800.0), (gemm, "GRBM_GUI_ACTIVE", 8 * 800.0),
+                     (torch_kernel, "GRBM_GUI_ACTIVE", 5.0)])
+    _counter_csv(b, [(gemm, "TCC_HIT_sum", 30.0), (gemm, "TCC_MISS_sum", 10.0)])
+    bench.counter_table([a, b])
+    out = capsys.readouterr().out
+    assert "`gemm_i8_kernel<(Epi)0, true>`" in out and "vectorized_elementwise" not in out
+    rows = {ln.split("|")[1].strip(): ln.split("|")[2].strip() for ln in out.splitlines() if ln.startswith("| ")}
+    assert rows["dispatches"] == "2"
+    assert float(rows["SQ_VALU_MFMA_BUSY_CYCLES"]) == pytest.approx(1024 * 400.0, rel=1e-3)
+    assert float(rows["*MFMA-busy fraction*"]) == pytest.approx(0.5)
+    assert float(rows["*L2 hit rate*"]) == pytest.approx(0.75)

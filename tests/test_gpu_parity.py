@@ -91,6 +91,57 @@ def test_quantize_int4_mismatch_rates_large_sample(cr, g):
         g, n, c.size, ns, sr.size))
 
 
+# Larger row counts (several persistent rounds of row groups, ragged last round) at K of 9..32
+# slots of 256 channels, even and odd log2 g; a zero row and one huge outlier in each.
+LARGE_QUANT_CASES = [
+    (1024, 5376, 256),
+    (1100, 2304, 128),
+    (1031, 4096, 2),
+    (1030, 6144, 32),
+    (2048, 5120, 128),
+    (1500, 8192, 256),
+]
+
+
+@pytest.mark.parametrize("rows,K,g", LARGE_QUANT_CASES)
+def test_quantize_int8_parity_many_rows(cr, rows, K, g):
+    P.say("quantize_act int8 rows=%d K=%d g=%d" % (rows, K, g))
+    x, _, _ = workloads.ragged_case(rows, K, 8, seed=rows + K + g)
+    x[3] = 0                    # a zero row: scale 0, codes 0
+    x[rows - 1, 5] = 3.0e4      # one huge outlier
+    q, s = cr.quantize_act(x.to(DEV), group=g, bits=8)
+    torch.cuda.synchronize()
+    qr, sr = orc.quantize_act_i8(_x64(x), g)
+    assert _np(s)[3] == 0 and np.all(_np(q)[3] == 0)
+    P.check_scales_f32(_np(s), sr)
+    P.check_codes(_np(q), qr)
+
+
+@pytest.mark.parametrize("rows,K,g", LARGE_QUANT_CASES)
+def test_quantize_bf16_and_fp32_inputs_agree(cr, rows, K, g):
+    """The same bf16 values given as fp32: the two input widths share every arithmetic step
+    after the load, so codes and scales are equal bit for bit."""
+    x, _, _ = workloads.ragged_case(rows, K, 8, seed=3 * rows + K + g)
+    xd = x.to(DEV)
+    q16, s16 = cr.quantize_act(xd, group=g, bits=8)
+    q32, s32 = cr.quantize_act(xd.float(), group=g, bits=8)
+    torch.cuda.synchronize()
+    assert torch.equal(q16, q32)
+    assert torch.equal(s16.view(torch.int32), s32.view(torch.int32))
+
+
+@pytest.mark.parametrize("g", [128, 256])
+def test_quantize_prefill_width_mismatch_rate_large_sample(cr, g):
+    """Rule (a) held to the rate itself on 5.5M codes at the prefill activations' K."""
+    x, _, _ = workloads.ragged_case(1024, 5376, 8, seed=99 + g)
+    q, s = cr.quantize_act(x.to(DEV), group=g, bits=8)
+    torch.cuda.synchronize()
+    qr, sr = orc.quantize_act_i8(_x64(x), g)
+    P.check_scales_f32(_np(s), sr)
+    n = P.check_codes(_np(q), qr, slack=False)
+    P.say("K=5376 g=%d: %d mismatches in %d codes" % (g, n, qr.size))
+
+
 def test_quantize_zero_rows_and_single_outlier(cr):
     x = torch.zeros(6, 512)
     x[1, 7] = 1000.0
