@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a4", "stack", "split", "copy"], default="all",
                     help="restrict the measured workloads (profiling runs); 'copy' = the counter calibration copy")
     ap.add_argument("--stack-layers", type=int, default=64)
+    ap.add_argument("--trace-table", metavar="KERNEL_TRACE_CSV",
+                    help="print markdown tables of kernel durations (per kernel, and per kernel x launch "
+                         "configuration) from a rocprofv3 --kernel-trace CSV and exit")
     ap.add_argument("--counter-table", nargs="+", metavar="CSV",
                     help="print a markdown table of per-dispatch mean counters per kernel from rocprofv3 --pmc "
                          "counter CSVs (one or more passes) and exit")
@@ -196,6 +199,14 @@ def bench_prefill(cr, wl, torch, steps, warmup):
         return e
 
     wall, marks = timed_loop(step, steps, warmup, torch)
+
+    # rotate+quantize alone, replayed from a HIP graph of 20 launches over the activation ring: the
+    # in-step event pair above also spans the dispatch of the kernel right after the previous GEMM
+    def rq_launch(i):
+        cr._call("convrot_quantize_act", xs[i % nx].data_ptr(), cr.CONVROT_DTYPE_BF16, M, K, 256, 8,
+                 xq.data_ptr(), xsc.data_ptr(), torch.cuda.current_stream(dev).cuda_stream)
+
+    t_rq_graph_us = graph_time_us(torch, rq_launch, 20, 20)
     t_rq = sum(m[0].elapsed_time(m[1]) for m in marks) / steps
     t_gemm = sum(m[1].elapsed_time(m[2]) for m in marks) / steps
     t_step = sum(m[0].elapsed_time(m[2]) for m in marks) / steps
@@ -203,7 +214,7 @@ def bench_prefill(cr, wl, torch, steps, warmup):
     rq_bytes = M * K * 2 + M * K + 4 * M
     gemm_bytes = M * K + N * K + 4 * M + 4 * N + 4 * N + 2 * M * N
     return dict(M=M, K=K, N=N, ops=ops, wall_ms=wall, step_ms=t_step, rq_ms=t_rq, gemm_ms=t_gemm,
-                rq_bytes=rq_bytes, gemm_bytes=gemm_bytes)
+                rq_graph_us=t_rq_graph_us, rq_bytes=rq_bytes, gemm_bytes=gemm_bytes)
 
 
 def bench_decode(cr, wl, torch, steps, warmup):
@@ -592,15 +603,13 @@ def _per_dispatch_kib(path, counter):
 
 PMC_COMMANDS = [
     "cd /tmp && export TMPDIR=/tmp && cd <repo>",
-    "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run --output-format csv -- "
-    "python bench.py --only prefill --steps 3 --warmup 1 --no-cpu-baseline",
-    "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run --output-format csv -- "
-    "python bench.py --only prefill --steps 3 --warmup 1 --no-cpu-baseline",
-    "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_cfetch -o run --output-format csv -- python bench.py --only copy",
-    "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_cwrite -o run --output-format csv -- python bench.py --only copy",
-    "python bench.py --pmc-summary gpurun_out/pmc_fetch/run_counter_collection.csv "
-    "gpurun_out/pmc_write/run_counter_collection.csv gpurun_out/pmc_cfetch/run_counter_collection.csv "
-    "gpurun_out/pmc_cwrite/run_counter_collection.csv",
+    "rocprofv3 --pmc FETCH_SIZE -d /tmp/pmc_fetch -o run --output-format csv -- "
+    "python3 bench.py --only prefill --steps 3 --warmup 1 --no-cpu-baseline",
+    "rocprofv3 --pmc WRITE_SIZE -d /tmp/pmc_write -o run --output-format csv -- "
+    "python3 bench.py --only prefill --steps 3 --warmup 1 --no-cpu-baseline",
+    "rocprofv3 --pmc FETCH_SIZE -d /tmp/pmc_cfetch -o run --output-format csv -- python3 bench.py --only copy",
+    "rocprofv3 --pmc WRITE_SIZE -d /tmp/pmc_cwrite -o run --output-format csv -- python3 bench.py --only copy",
+    "python3 bench.py --pmc-summary <the four run_counter_collection.csv files, in the order above>",
 ]
 
 
@@ -629,12 +638,21 @@ def counter_table(paths):
     SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs); L2 hit rate =
     TCC_HIT / (TCC_HIT + TCC_MISS); mean L2 read latency seen by the L1 = TCP_TCC_READ_REQ_LATENCY /
     TCP_TCC_READ_REQ (cycles)."""
-    acc = {}
+    acc, by_cfg = {}, {}
     for path in paths:
-        for name, cname, v in _counter_rows(path):
-            if not any(k in name for k in COUNTER_KERNELS):
-                continue
-            acc.setdefault(_kernel_label(name), {}).setdefault(cname, []).append(v)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                if not any(k in name for k in COUNTER_KERNELS):
+                    continue
+                v = float(r["Counter_Value"])
+                acc.setdefault(_kernel_label(name), {}).setdefault(r["Counter_Name"], []).append(v)
+                try:
+                    cfg = (_kernel_label(name), int(_col(r, "Grid_Size", "Grid_Size_X")),
+                           int(_col(r, "Workgroup_Size", "Workgroup_Size_X")))
+                except (KeyError, ValueError):
+                    continue
+                by_cfg.setdefault(cfg, {}).setdefault(r["Counter_Name"], []).append(v)
     kernels = sorted(acc)
     counters = sorted({c for k in kernels for c in acc[k]})
     mean = {k: {c: statistics.fmean(v) for c, v in acc[k].items()} for k in kernels}
@@ -657,6 +675,49 @@ def counter_table(paths):
     derived("MFMA-busy fraction", lambda m: m["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * m["GRBM_GUI_ACTIVE"] / 8))
     derived("L2 hit rate", lambda m: m["TCC_HIT_sum"] / (m["TCC_HIT_sum"] + m["TCC_MISS_sum"]))
     derived("mean L2 read latency (cycles)", lambda m: m["TCP_TCC_READ_REQ_LATENCY_sum"] / m["TCP_TCC_READ_REQ_sum"])
+    if len(by_cfg) > len(kernels):
+        # the same kernel at several launch shapes: one row per kernel x grid x workgroup size
+        cnames = sorted({c for d in by_cfg.values() for c in d})
+        print()
+        print("| kernel | grid threads | workgroup threads | dispatches | " + " | ".join(cnames) + " |")
+        print("|---|---|---|---|" + "---|" * len(cnames))
+        for (k, grid, wg), d in sorted(by_cfg.items()):
+            print("| `%s` | %d | %d | %d | " % (k, grid, wg, max(len(v) for v in d.values())) +
+                  " | ".join("%.4g" % statistics.median(d[c]) if c in d else "" for c in cnames) + " |")
+
+
+def _col(row, *names):
+    for n in names:
+        if n in row and row[n] != "":
+            return row[n]
+    raise KeyError(names[0])
+
+
+def trace_table(path):
+    """Kernel durations from a rocprofv3 kernel-trace CSV: calls, mean, median, min and max per
+    kernel (all of them, longest total first), then per kernel x grid x workgroup size for this
+    library's kernels."""
+    per, per_cfg = {}, {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = _kernel_label(r["Kernel_Name"])
+            us = (int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))) * 1e-3
+            per.setdefault(name, []).append(us)
+            if any(k in r["Kernel_Name"] for k in COUNTER_KERNELS):
+                grid = int(_col(r, "Grid_Size", "Grid_Size_X"))
+                wg = int(_col(r, "Workgroup_Size", "Workgroup_Size_X"))
+                per_cfg.setdefault((name, grid, wg), []).append(us)
+    print("| kernel | calls | mean us | median us | min us | max us |")
+    print("|---|---|---|---|---|---|")
+    for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        print("| `%s` | %d | %.2f | %.2f | %.2f | %.2f |" % (name, len(v), statistics.fmean(v), statistics.median(v),
+                                                             min(v), max(v)))
+    print()
+    print("| kernel | grid threads | workgroup threads | calls | mean us | median us | min us | max us |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (name, grid, wg), v in sorted(per_cfg.items(), key=lambda kv: (kv[0][0], -len(kv[1]))):
+        print("| `%s` | %d | %d | %d | %.2f | %.2f | %.2f | %.2f |" % (
+            name, grid, wg, len(v), statistics.fmean(v), statistics.median(v), min(v), max(v)))
 
 
 def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
@@ -695,6 +756,9 @@ def main():
     if args.counter_table:
         counter_table(args.counter_table)
         return
+    if args.trace_table:
+        trace_table(args.trace_table)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -713,8 +777,9 @@ def main():
     if args.only in ("all", "prefill"):
         res["prefill"] = bench_prefill(cr, wl, torch, args.steps, args.warmup)
         p = res["prefill"]
-        log("prefill: step %.1f us (rotate+quant %.1f us, GEMM %.1f us), wall %.1f us" % (
-            p["step_ms"] * 1e3, p["rq_ms"] * 1e3, p["gemm_ms"] * 1e3, p["wall_ms"] * 1e3))
+        log("prefill: step %.1f us (rotate+quant %.1f us in the step, %.1f us per graph-replayed launch; GEMM "
+            "%.1f us), wall %.1f us" % (p["step_ms"] * 1e3, p["rq_ms"] * 1e3, p["rq_graph_us"], p["gemm_ms"] * 1e3,
+                                       p["wall_ms"] * 1e3))
         torch.cuda.empty_cache()
     if args.only in ("all", "decode"):
         res["decode"] = bench_decode(cr, wl, torch, args.steps, args.warmup)
@@ -761,6 +826,8 @@ def main():
                          "algorithmic_bytes": p["gemm_bytes"], "source_hash": h},
             "kernels": {"rotate_quant_us": p["rq_ms"] * 1e3, "rotate_quant_GBps": rq_gbs,
                         "rotate_quant_frac_hbm": rq_gbs / PEAK_HBM_GBS,
+                        "rotate_quant_graph_us": p["rq_graph_us"],
+                        "rotate_quant_graph_frac_hbm": p["rq_bytes"] / (p["rq_graph_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
                         "rotate_quant_traffic": traffic_from_profiles("rotate_quant_prefill",
                                                                       src_hash("rotate_quant.hip")),
                         "gemm_us": p["gemm_ms"] * 1e3, "gemm_TOPs": gemm_tops,

@@ -87,3 +87,18 @@ def test_counter_table_means_and_derived_rows(tmp_path, capsys):
     assert float(rows["SQ_VALU_MFMA_BUSY_CYCLES"]) == pytest.approx(1024 * 400.0, rel=1e-3)
     assert float(rows["*MFMA-busy fraction*"]) == pytest.approx(0.5)
     assert float(rows["*L2 hit rate*"]) == pytest.approx(0.75)
+
+
+def test_trace_table_groups_by_kernel_and_launch_shape(tmp_path, capsys):
+    path = tmp_path / "kernel_trace.csv"
+    gemm = "void convrot::(anonymous namespace)::gemm_i8_kernel<(convrot::Epi)0, true>(convrot::(anonymous namespace)::GemmParams)"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Workgroup_Size", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for i, (dur, grid) in enumerate([(300000, 131072), (310000, 131072), (20000, 4096)]):
+            w.writerow({"Kernel_Name": gemm, "Grid_Size": grid, "Workgroup_Size": 512,
+                        "Start_Timestamp": 1000 * i, "End_Timestamp": 1000 * i + dur})
+    bench.trace_table(str(path))
+    out = capsys.readouterr().out
+    assert "| `gemm_i8_kernel<(Epi)0, true>` | 3 | 210.00 | 300.00 | 20.00 | 310.00 |" in out
+    assert "| `gemm_i8_kernel<(Epi)0, true>` | 131072 | 512 | 2 | 305.00 |" in out
