@@ -315,6 +315,16 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
         }
     };
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+    // Inside one scheduling region, the next K-step's fragment reads go out two at a time between
+    // this K-step's MFMAs (sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read), so the matrix
+    // pipe gets its next instruction without queueing behind a burst of reads.
+    auto interleave_reads = [] {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+    };
 
     // Fold of a group into facc (zeroed at the tile's start): facc += gacc * sx[m] * sw[n].
     // Lane holds token m = lane%32 of block (bi, bj) and weight rows n = 8*(v/4) + 4*(lane/32) + v%4.
@@ -457,9 +467,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
         }
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (g + NST < total) issue(g + NST);
-        if (g + 1 < total) read_frags(g + 1, 0, 0);
         fence();
+        // (after the stream's last K-tile this reads a stage whose fragments are never used)
+        read_frags(g + 1, 0, 0);
         mfmas(1);
+        interleave_reads();
         fence();
         ++g;
     };
@@ -476,8 +488,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
         tail(t, 0);
         if constexpr (GKT == 2) {
             read_frags(g, 1, 1);
-            fence();
             mfmas(0);
+            interleave_reads();
             tail(t, 1);
         }
         ++gidx;
@@ -487,8 +499,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_w4a4_kernel(W4Params p)
             tail(t, GKT * gi);
             if constexpr (GKT == 2) {
                 read_frags(g, 1, 1);
-                fence();
                 mfmas(0);
+                interleave_reads();
                 tail(t, 2 * gi + 1);
             }
             ++gidx;
