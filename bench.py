@@ -628,8 +628,8 @@ def _kernel_label(name: str) -> str:
     return n[:cut]
 
 
-COUNTER_KERNELS = ("gemm_i8_kernel", "gemm_w4a4_kernel", "rotate_quant_kernel", "tile_fp6_kernel", "gemv_i8_kernel",
-                   "gemv_w4a8_kernel", "split_reduce_kernel")
+COUNTER_KERNELS = ("gemm_i8_kernel", "gemm_w4a4_kernel", "rotate_quant_kernel", "rotate_quant_fp6_kernel",
+                   "tile_fp6_kernel", "gemv_i8_kernel", "gemv_w4a8_kernel", "split_reduce_kernel")
 
 
 def counter_table(paths):

@@ -152,7 +152,9 @@ int convrot_linear_noalloc(const void *x, int x_dtype, const int8_t *xq, const f
 /*
  * W4A4 ConvRot linear (nvfp4-convrot page, section 五): both operands rotated, INT4 per
  * (row, group) with fp16 scales, per-group integer dot products scaled and summed in fp32.
- *   x bf16/fp32 [M, K] quantized into the workspace, or x = NULL and the caller's
+ *   x bf16/fp32 [M, K] rotated and quantized into the workspace (straight into the FP6
+ *   matrix-core order; the same codes and scales convrot_quantize_act(bits = 4) gives, so the
+ *   result is bit-identical to passing those), or x = NULL and the caller's
  *   xq uint8 [M, K/2] / x_scale fp16 [K/group, M] from convrot_quantize_act(bits = 4).
  *   The workspace (convrot_workspace_bytes(M, N, K, 4)) is required in both cases.
  *   wq uint8 [N, K/2], w_scale fp16 [K/group, N] from convrot_prepare_weight(bits = 4).

@@ -371,17 +371,18 @@ int linear_w4a4(const char *who, const void *x, int x_dtype, const uint8_t *xq, 
     if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
         return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes", who, L.total);
     if ((rc = check_device())) return rc;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
     if (x) {
-        uint8_t *ws = static_cast<uint8_t *>(workspace);
-        rc = hip_status(convrot::launch_rotate_quant(x, x_dtype == CONVROT_DTYPE_F32, M, (int)K, log2i(group), 4, ws + L.xq,
-                                                     ws + L.xs, stream),
-                        "rotate_quant");
+        // rotate + quantize straight into the GEMM's FP6 token tiles (no packed INT4 copy)
+        rc = hip_status(convrot::launch_rotate_quant_fp6(x, x_dtype == CONVROT_DTYPE_F32, M, (int)K, log2i(group),
+                                                         ws + L.tiles, ws + L.xs, stream),
+                        "rotate_quant_fp6");
         if (rc) return rc;
-        xq = ws + L.xq;
+        xq = ws + L.tiles;
         x_scale = reinterpret_cast<const uint16_t *>(ws + L.xs);
     }
-    return hip_status(convrot::launch_gemm_w4a4(xq, w, w_tiled, x_scale, w_scale, bias, y, convrot::Epi::Bf16, M, N,
-                                                (int)K, group, static_cast<uint8_t *>(workspace) + L.tiles, stream),
+    return hip_status(convrot::launch_gemm_w4a4(xq, x != nullptr, w, w_tiled, x_scale, w_scale, bias, y,
+                                                convrot::Epi::Bf16, M, N, (int)K, group, ws + L.tiles, stream),
                       "gemm_w4a4");
 }
 
@@ -545,7 +546,7 @@ int convrot_gemm_i4_i32(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t
     if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
         return fail(CONVROT_ERR_WORKSPACE, "%s: need a 256-byte aligned workspace of %zu bytes", who, L.total);
     if ((rc = check_device())) return rc;
-    return hip_status(convrot::launch_gemm_w4a4(xq, wq, false, nullptr, nullptr, nullptr, acc, convrot::Epi::Int32, M, N,
+    return hip_status(convrot::launch_gemm_w4a4(xq, false, wq, false, nullptr, nullptr, nullptr, acc, convrot::Epi::Int32, M, N,
                                                 (int)K, 256, static_cast<uint8_t *>(workspace) + L.tiles, stream),
                       "gemm_w4a4");
 }

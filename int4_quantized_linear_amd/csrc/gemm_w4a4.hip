@@ -544,7 +544,7 @@ hipError_t launch_tile_w4a4(const uint8_t *q, int64_t R, int K, uint8_t *out, hi
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_w4a4(const uint8_t *xq, const uint8_t *wq, bool w_tiled, const uint16_t *sx,
+hipError_t launch_gemm_w4a4(const uint8_t *xq, bool x_tiled, const uint8_t *wq, bool w_tiled, const uint16_t *sx,
                             const uint16_t *sw, const float *bias, void *y, Epi epi, int64_t M, int64_t N, int K,
                             int group, void *ws, hipStream_t stream)
 {
@@ -556,12 +556,16 @@ hipError_t launch_gemm_w4a4(const uint8_t *xq, const uint8_t *wq, bool w_tiled, 
     // scale groups of 2 K-tiles (256 channels) or 1 (128); at least 2 K-tiles (bias ring)
     const int gkt = group / BK;
     if ((gkt != 1 && gkt != 2) || K % group || K < 2 * BK) return hipErrorInvalidValue;
-    uint8_t *xt = static_cast<uint8_t *>(ws);
-    hipError_t e = launch_tile_w4a4(xq, M, K, xt, stream);
-    if (e != hipSuccess) return e;
+    uint8_t *xt_ws = static_cast<uint8_t *>(ws);
+    const uint8_t *xt = xq;
+    hipError_t e = hipSuccess;
+    if (!x_tiled) {
+        if ((e = launch_tile_w4a4(xq, M, K, xt_ws, stream)) != hipSuccess) return e;
+        xt = xt_ws;
+    }
     const uint8_t *wt = wq;
     if (!w_tiled) {
-        uint8_t *wt_ws = xt + row_blocks(M) * (K / 64) * PIECE;
+        uint8_t *wt_ws = xt_ws + row_blocks(M) * (K / 64) * PIECE;
         if ((e = launch_tile_w4a4(wq, N, K, wt_ws, stream)) != hipSuccess) return e;
         wt = wt_ws;
     }

@@ -11,6 +11,10 @@ namespace convrot {
 // bits 8 -> q int8 [rows, K], scale fp32 [rows]; bits 4 -> q uint8 [rows, K/2], scale fp16 [rows, K/256].
 hipError_t launch_rotate_quant(const void *x, bool x_f32, int64_t rows, int K, int log2g, int bits, void *q,
                                void *scale, hipStream_t stream);
+// The INT4 case (log2g 7 or 8, K % 128 == 0) written straight as the FP6 tiles of the W4A4 GEMM:
+// tiles of w4a4_tiled_bytes(rows, 0, K) bytes (rows padded to 32 with zero codes), scale as above.
+hipError_t launch_rotate_quant_fp6(const void *x, bool x_f32, int64_t rows, int K, int log2g, uint8_t *tiles,
+                                   void *scale, hipStream_t stream);
 
 // Epilogue selector of the integer GEMM / GEMV kernels.
 enum class Epi { Bf16 = 0, Int32 = 1 };
@@ -34,13 +38,14 @@ hipError_t launch_gemv_i8(const int8_t *xq, const int8_t *wq, const float *sx, c
 // W4A4: y = bf16(sum_g acc_g * sx[m,g] * sw[n,g] + bias[n]) with packed int4 operands and
 // fp16 group scales (group = 256 or 128, K % group == 0, K >= 256), or the unscaled int32 total
 // sum_k cx*cw (scales ignored).
-// Both operands run through the FP6 tiles of launch_tile_w4a4; the weights are re-encoded
-// into `ws` on every call, unless w_tiled says wq already holds their tiles.  `ws` is scratch
-// of w4a4_tiled_bytes(M, w_tiled ? 0 : N, K) bytes (16-byte aligned).
+// Both operands run through the FP6 tiles of launch_tile_w4a4: the tokens are re-encoded into
+// the start of `ws` unless x_tiled says xq already holds their tiles (launch_rotate_quant_fp6),
+// the weights after them unless w_tiled says wq does.  `ws` is scratch of
+// w4a4_tiled_bytes(M, w_tiled ? 0 : N, K) bytes (16-byte aligned).
 size_t w4a4_tiled_bytes(int64_t M, int64_t N, int K);
 // Packed int4 rows [R, K/2] -> FP6 tiles (w4a4_tiled_bytes(R, 0, K) bytes), K % 128 == 0.
 hipError_t launch_tile_w4a4(const uint8_t *q, int64_t R, int K, uint8_t *out, hipStream_t stream);
-hipError_t launch_gemm_w4a4(const uint8_t *xq, const uint8_t *wq, bool w_tiled, const uint16_t *sx,
+hipError_t launch_gemm_w4a4(const uint8_t *xq, bool x_tiled, const uint8_t *wq, bool w_tiled, const uint16_t *sx,
                             const uint16_t *sw, const float *bias, void *y, Epi epi, int64_t M, int64_t N, int K,
                             int group, void *ws, hipStream_t stream);
 

@@ -109,9 +109,10 @@ __device__ __forceinline__ void fwht_slot(float (&v)[4][8], int qd)
 // an out-of-bounds offset (loads return 0, stores are dropped): no branches around them, so the
 // loads of a wavefront are all in flight together.
 //
-// Persistent: a workgroup walks row groups blockIdx.x, blockIdx.x + gridDim.x, ... and issues
-// the raw loads of its next row group before it transforms the current one, so HBM reads stay
-// in flight while the VALU works (without this, all waves would load, then all compute).
+// Persistent: a workgroup walks row groups blockIdx.x, blockIdx.x + gridDim.x, ...  Two
+// workgroups share a CU (the grid holds about RQ_WAVES_PER_CU wavefronts per CU), so one's loads
+// are in flight while the other transforms; carrying the next row group's loads in registers
+// instead costs enough registers to halve that and is slower.
 template <bool F32IN, int BITS, int SETS, int LG>
 __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
 {
@@ -163,14 +164,10 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
                 }
     };
 
-    // Prefetching holds a second copy of the raw row data: only for SETS == 1 (K <= 32768); the
-    // wider rows would not fit the registers of a 1024-thread workgroup.
-    constexpr bool PF = SETS == 1;
     int it = blockIdx.x;
     int par = 0;
-    if (PF && it < p.ngroups) issue(it);
     for (; it < p.ngroups; it += gridDim.x, par ^= 1) {
-        if constexpr (!PF) issue(it);
+        issue(it);
         const int64_t row0 = (int64_t)it * R;
         const int nrows = (int)(p.rows - row0 < R ? p.rows - row0 : R);
         float v[SETS][4][8];
@@ -189,7 +186,6 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
                     }
                 }
             }
-        if (PF && it + (int)gridDim.x < p.ngroups) issue(it + gridDim.x);   // prefetch the next group
         bool ok[SETS];
 #pragma unroll
         for (int s = 0; s < SETS; ++s) ok[s] = rr[s] < nrows;
@@ -309,7 +305,181 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
     }
 }
 
-constexpr int RQ_WAVES_PER_CU = 16;
+// ---------------------------------------------------------------------------------------------
+// INT4 straight into the FP6 tiles of the W4A4 GEMM.  Same rotation, scales and codes as the
+// BITS = 4 kernel above (the 4-bit scale group is a slot or half a slot, so no reduction leaves
+// a slot), but the codes are written as the E3M2 pieces the GEMM streams (gemm_w4a4.hip: per
+// 32-row block and 64-channel K-step a 1536-byte piece; lane l = (row r = l % 32, half h = l / 32)
+// owns the 32 codes at channels 64 ks + 32 h + s, 6 bits each at bit 6 s of a 24-byte string
+// whose bytes 0..15 sit at 16 l and 16..23 at 1024 + 8 l; rows past the matrix are zeros).
+//
+// Work unit: one 32-row block x one 256-channel block, a 256-thread workgroup, so that all of a
+// piece's cache lines are written by one CU.  Wavefront w takes rows 8 w .. 8 w + 7, one slot
+// (row) per lane bits 4:2 and the in-slot layout of the kernel above.  After the butterflies, lane
+// (qd, h) holds, in register r, 8 codes of K-step 4 j + r at s = 8 qd .. 8 qd + 7 of half h
+// (once the lane halves are swapped back), i.e. 48 bits at bit 48 qd of lane string l.  One
+// v_cvt_scalef32_2xpk16_bf6_f32 turns the lane's 32 integer-valued floats into 6 dwords of E3M2
+// (position 2i from the first source's element i, 2i + 1 from the second's; scale 1: exact for
+// integers up to 8 in magnitude), ordered so that dwords 0..2 hold registers 0 and 2 and dwords
+// 3..5 registers 1 and 3: the swap of lane halves then runs on whole dwords.  Each lane stores its
+// 48 bits of each K-step as one dword and one short.
+//
+// Rows from the matrix's end up to the next multiple of 32 read zeros (past num_records) and
+// write zero codes; their scales are not stored.
+
+struct RQ6Params {
+    const void *x;
+    uint8_t *tiles;      // [ceil(rows / 32)][K / 64][1536]
+    __half *scale;       // [K / g, rows]
+    int64_t rows;
+    int K;
+    int nblk;            // ceil(K / 256)
+    float cg;
+    double root;
+};
+
+typedef unsigned v6u __attribute__((ext_vector_type(6)));
+
+template <bool F32IN, int LG>
+__global__ void __launch_bounds__(256) rotate_quant_fp6_kernel(RQ6Params p)
+{
+    constexpr int PIECE = 1536;
+    constexpr int ES = F32IN ? 4 : 2;
+    constexpr int NL = F32IN ? 2 : 1;
+    constexpr int HS = LG == 7 ? 2 : 1;                    // scale groups per slot
+    const int lane = threadIdx.x & 63;
+    const int qd = lane & 3, h = lane >> 5, sl = (lane >> 2) & 7;
+    const int rw = 8 * (threadIdx.x >> 6) + sl;           // row inside the 32-row block
+    const int K = p.K, KS = K >> 6;
+    const uint32_t u = blockIdx.x;
+    const uint32_t rb = u / (uint32_t)p.nblk, j = u - rb * (uint32_t)p.nblk;
+    const int64_t row0 = 32 * (int64_t)rb;
+    const int nrows = (int)(p.rows - row0 < 32 ? p.rows - row0 : 32);
+
+    // loads: 4 chunks of 8 channels (rows past the matrix lie past num_records and read zeros;
+    // the second half of a 128-channel last block is out of range too)
+    v4u raw[4][NL];
+    {
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(static_cast<const uint8_t *>(p.x) + row0 * K * ES), (short)0, nrows * K * ES,
+            0x00020000);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int k = 256 * (int)j + 64 * r + 32 * h + 8 * qd;
+            const uint32_t o = (rw < nrows && k < K) ? (uint32_t)(rw * K + k) * ES : OOB;
+#pragma unroll
+            for (int q = 0; q < NL; ++q)
+                raw[r][q] = __builtin_amdgcn_raw_buffer_load_b128(rx, o == OOB ? OOB : o + 16 * q, 0, 2);
+        }
+    }
+    float v[4][8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if constexpr (F32IN) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[r][e] = __uint_as_float(raw[r][e >> 2][e & 3]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[r][2 * e] = bf16lo_to_f32(raw[r][0][e]);
+                v[r][2 * e + 1] = bf16hi_to_f32(raw[r][0][e]);
+            }
+        }
+    }
+
+    fwht_slot<LG>(v, qd);
+
+    // per scale group: absmax over the slot's 8 lanes, fp16 scale, code multiplier (with the sign
+    // the lane-exchange stages left on this lane)
+    const float lsign = ((qd ^ (qd >> 1)) & 1) ? -1.0f : 1.0f;
+    float mult[HS];
+#pragma unroll
+    for (int hs = 0; hs < HS; ++hs) {
+        float a = 0.0f;
+#pragma unroll
+        for (int r = hs * (4 / HS); r < (hs + 1) * (4 / HS); ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(v[r][e]));
+        a = __builtin_fmaxf(a, dpp_xor1(a));
+        a = __builtin_fmaxf(a, dpp_xor2(a));
+        uint32_t lo = __float_as_uint(a), hi = lo;
+        swap32(lo, hi);
+        a = __builtin_fmaxf(__uint_as_float(lo), __uint_as_float(hi));
+        const float an = LG % 2 == 0 ? a * p.cg : (float)((double)a / p.root);
+        const __half sh = f16_quotient_rne(an, 7.0f);
+        const float sc = __half2float(sh);
+        mult[hs] = sc > 0.0f ? lsign * (p.cg / sc) : 0.0f;
+        const int64_t grp = (int64_t)j * HS + hs;
+        if (rw < nrows && qd == 0 && h == 0 && grp * (256 / HS) < K) p.scale[grp * p.rows + row0 + rw] = sh;
+    }
+
+    // integer-valued codes (one rounding, as rne_bits) in the conversion's source order:
+    // output position 2i + b <- source b element i; positions 0..7 register 0, 8..15 register 2,
+    // 16..23 register 1, 24..31 register 3
+    v16f src[2];
+#pragma unroll
+    for (int pos = 0; pos < 32; ++pos) {
+        const int r = (pos >> 4) | ((pos >> 2) & 2), e = pos & 7;
+        src[pos & 1][pos >> 1] = __builtin_fmaf(v[r][e], mult[r / (4 / HS)], kMagicRound) - kMagicRound;
+    }
+    const v6u d = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(src[0], src[1], 1.0f);
+    uint32_t dw[6] = {d[0], d[1], d[2], d[3], d[4], d[5]};
+    // lane halves back: afterwards dwords 0..2 hold K-steps 0 and 2, dwords 3..5 K-steps 1 and 3
+#pragma unroll
+    for (int i = 0; i < 3; ++i) swap32(dw[i], dw[i + 3]);
+
+    // this lane's 6 bytes of each K-step's string (bytes 6 qd .. 6 qd + 5) as one dword and one
+    // short; K-steps past K lie past num_records
+    const uint32_t l = (uint32_t)rw + 32u * (uint32_t)h;
+    const uint32_t o32 = qd == 0 ? 16u * l : qd == 1 ? 16u * l + 8u : qd == 2 ? 16u * l + 12u : 1028u + 8u * l;
+    const uint32_t o16 = qd == 0 ? 16u * l + 4u : qd == 1 ? 16u * l + 6u : qd == 2 ? 1024u + 8u * l : 1026u + 8u * l;
+    const bool odd = qd & 1;
+    const int nks = KS - 4 * (int)j < 4 ? KS - 4 * (int)j : 4;
+    const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+        p.tiles + ((int64_t)rb * KS + 4 * (int64_t)j) * PIECE, (short)0, nks * PIECE, 0x00020000);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        // the 48-bit string of K-step ks: low dword c0, high half c1 (low 16 bits)
+        const uint32_t *b = dw + 3 * (ks & 1);
+        const uint32_t c0 = ks < 2 ? b[0] : __builtin_amdgcn_alignbit(b[2], b[1], 16);
+        const uint32_t c1 = ks < 2 ? b[1] : b[2] >> 16;
+        const uint32_t w32 = odd ? __builtin_amdgcn_alignbit(c1, c0, 16) : c0;
+        const uint32_t w16 = odd ? c0 : c1;
+        __builtin_amdgcn_raw_buffer_store_b32(w32, rt, o32 + ks * PIECE, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)w16, rt, o16 + ks * PIECE, 0, 0);
+    }
+}
+
+hipError_t launch_rotate_quant_fp6(const void *x, bool x_f32, int64_t rows, int K, int log2g, uint8_t *tiles,
+                                   void *scale, hipStream_t stream)
+{
+    if (rows <= 0) return hipSuccess;
+    if ((log2g != 7 && log2g != 8) || K % 128 || K < 128) return hipErrorInvalidValue;
+    RQ6Params p;
+    p.x = x;
+    p.tiles = tiles;
+    p.scale = static_cast<__half *>(scale);
+    p.rows = rows;
+    p.K = K;
+    p.nblk = (K + 255) / 256;
+    const int64_t units = ((rows + 31) / 32) * p.nblk;
+    if (units >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    p.root = __builtin_sqrt((double)(1 << log2g));
+    p.cg = (float)(1.0 / p.root);
+    // one workgroup per unit: ~40 resident wavefronts per CU at this kernel's register count (a
+    // persistent grid with the next unit's loads in flight holds fewer and is slower)
+    const dim3 grid((unsigned)units), block(256);
+    if (x_f32) {
+        if (log2g == 8) hipLaunchKernelGGL((rotate_quant_fp6_kernel<true, 8>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((rotate_quant_fp6_kernel<true, 7>), grid, block, 0, stream, p);
+    } else {
+        if (log2g == 8) hipLaunchKernelGGL((rotate_quant_fp6_kernel<false, 8>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((rotate_quant_fp6_kernel<false, 7>), grid, block, 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
+constexpr int RQ_WAVES_PER_CU = 32;
 
 // Host-side launch geometry: rows per workgroup and wavefronts per workgroup so that the
 // 8 slots per wavefront are used as fully as possible (<= 16 wavefronts, <= 64 rows).

@@ -540,6 +540,33 @@ def test_linear_w4a4_packed_matches(cr, M, N, K, g):
     P.check_y(_x64(y4), yown, "y (no bias, own codes)", strict_frac=1e-4)
 
 
+FUSED_W4_CASES = [(M, K, g) for M in (1, 31, 33, 100) for K, g in ((256, 256), (384, 128), (2688, 128), (5376, 256))]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,K,g", FUSED_W4_CASES)
+def test_linear_w4a4_x_given_matches_codes_path(cr, M, K, g, dtype):
+    """With x given, the W4A4 linear rotates and quantizes straight into the GEMM's FP6 token tiles
+    (rows padded to the 32-row block with zero codes); the result must equal, bit for bit, the
+    linear on the packed INT4 codes and fp16 scales that quantize_act makes from the same x."""
+    N = 72
+    P.say("linear_w4a4 x given vs codes M=%d N=%d K=%d g=%d %s" % (M, N, K, g, dtype))
+    x, w, b = workloads.ragged_case(M, K, N, seed=9, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    wq, ws = cr.prepare_weight(wd, g, 4)
+    wp = cr.pack_weight_w4a4(wq)
+    xq, xs = cr.quantize_act(xd, g, 4)
+    y_x = cr.linear_w4a4(xd, wq, ws, bd, group=g)
+    y_q = cr.linear_w4a4(None, wq, ws, bd, group=g, xq=xq, x_scale=xs)
+    yp_x = cr.linear_w4a4_packed(xd, wp, ws, None, group=g)
+    yp_q = cr.linear_w4a4_packed(None, wp, ws, None, group=g, xq=xq, x_scale=xs)
+    torch.cuda.synchronize()
+    assert torch.equal(y_x, y_q)
+    assert torch.equal(yp_x, yp_q)
+    yown = orc.linear_i4(orc.unpack_i4(_np(xq)), _np(xs).T, orc.unpack_i4(_np(wq)), _np(ws).T, b.numpy(), g)
+    P.check_y(_x64(y_x), yown, "y (own codes)", strict_frac=1e-4)
+
+
 def _w4a4_case(cr, x, w, b, g):
     xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
     wq, ws = cr.prepare_weight(wd, g, 4)
