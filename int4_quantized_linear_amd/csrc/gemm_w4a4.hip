@@ -12,7 +12,8 @@
 // the fp16 scales are applied afterwards in fp32, group by group in increasing order.
 //
 // Two kernels:
-//  * tile: packed nibbles -> FP6 in the order the MFMA consumes them.  Per 32-row block and
+//  * tile: packed nibbles -> FP6 in the order the MFMA consumes them (weights once, or tokens
+//    given as packed codes).  Per 32-row block and
 //    64-channel K-step one 1536-byte piece; lane l = (r = l % 32, h = l / 32) owns the 32 codes
 //    of row r at channels 64 ks + 32 h + s (s = 0..31), 6 bits each at bit 6 s of a 24-byte
 //    string whose first 16 bytes sit at 16 l and last 8 at 1024 + 8 l.  Pieces are ordered
@@ -62,20 +63,6 @@ constexpr int GROUP_M = 8;
 constexpr uint32_t OOB = 0x80000000u;
 constexpr int NUM_RECORDS = 0x7ffffff0;
 
-// E3M2 bit patterns of the 4-bit codes: nibble v is the code v (v < 8) or v - 16 (v >= 8).
-constexpr uint32_t e3m2_of_magnitude(int a)   // a = 0..8
-{
-    return a == 0 ? 0u : a == 1 ? 12u : a == 2 ? 16u : a == 3 ? 18u : a == 4 ? 20u : a == 5 ? 21u : a == 6 ? 22u
-                                                                                        : a == 7 ? 23u : 24u;
-}
-constexpr uint64_t e3m2_table(bool negative)   // 8 entries of 6 bits: nibbles 0..7 or 8..15
-{
-    uint64_t t = 0;
-    for (int i = 0; i < 8; ++i)
-        t |= (uint64_t)(negative ? 0x20u | e3m2_of_magnitude(8 - i) : e3m2_of_magnitude(i)) << (6 * i);
-    return t;
-}
-constexpr uint64_t E3M2_POS = e3m2_table(false), E3M2_NEG = e3m2_table(true);
 
 struct W4Params {
     const uint8_t *xt;    // tokens, FP6 tiles [ceil(M/32)][K/64][1536]
@@ -115,47 +102,58 @@ __device__ __forceinline__ v16f mfma_fp6(const v8i &a, const v8i &b, const v16f 
 }
 
 // ---------------------------------------------------------------------------------------------
-// tile: a workgroup re-encodes 32 rows x 256 channels (4 pieces) per step.  Thread t reads the
+// tile: a workgroup re-encodes 32 rows x 256 channels (4 pieces) per unit.  Thread t reads the
 // 16 packed bytes (32 codes) of row t/8 at channel chunk t%8, so a wavefront reads 8 whole
 // 128-byte lines, and those 32 codes are exactly what lane (row, chunk%2) of piece (chunk/2)
-// holds: 24 bytes out.  A byte's two nibbles become their two 6-bit codes (12 bits) through a
-// 256-entry table in LDS.  K % 128 == 0: with K % 256 == 128 a row block's last step has only
-// 2 pieces, and the threads of the other two do nothing.
+// holds: 24 bytes out.  The codes become integer-valued floats (sign-extending bit-field
+// extracts) and one v_cvt_scalef32_2xpk16_bf6_f32 packs them as E3M2 (output position 2i + b
+// from element i of source b: the even channels, i.e. the low nibbles, are source 0; scale 1,
+// exact for integers up to 8 in magnitude).  A thread takes TILE_U units per iteration with all
+// their loads in flight first.  Out-of-range rows and channels lie past num_records: they read
+// zeros and their stores drop.  K % 128 == 0: with K % 256 == 128 a row block's last unit has
+// only 2 pieces.
+
+constexpr int TILE_U = 2;
 
 __global__ void __launch_bounds__(256) tile_fp6_kernel(const uint8_t *src, uint8_t *dst, int64_t R, int K,
                                                        uint32_t units)
 {
-    __shared__ uint32_t lut[256];   // byte -> E3M2(low nibble) | E3M2(high nibble) << 6
-    {
-        const uint32_t b = threadIdx.x, lo = b & 15u, hi = b >> 4;
-        const uint32_t clo = (uint32_t)(((lo & 8u) ? E3M2_NEG : E3M2_POS) >> (6 * (lo & 7u))) & 63u;
-        const uint32_t chi = (uint32_t)(((hi & 8u) ? E3M2_NEG : E3M2_POS) >> (6 * (hi & 7u))) & 63u;
-        lut[b] = clo | (chi << 6);
-    }
-    __syncthreads();
     const uint32_t KS = (uint32_t)K >> 6, KQ = ((uint32_t)K + 255) >> 8;
     const uint32_t r = threadIdx.x >> 3, c = threadIdx.x & 7;
     const uint32_t l = r + 32 * (c & 1);                     // lane of the piece
-    for (uint32_t u = blockIdx.x; u < units; u += gridDim.x) {
-        const uint32_t rb = u / KQ, q = u - rb * KQ;
-        const uint32_t ks = 4 * q + (c >> 1);                   // K-step of this thread's piece
-        if (ks >= KS) continue;                                  // past K (K % 256 == 128)
-        const int64_t row = 32 * (int64_t)rb + r;
-        v4u d = {0u, 0u, 0u, 0u};
-        if (row < R)
-            d = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(src + row * (K >> 1) + 128 * q + 16 * c));
-        uint32_t o[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+    for (uint32_t u0 = blockIdx.x; u0 < units; u0 += TILE_U * gridDim.x) {
+        v4u d[TILE_U];
 #pragma unroll
-        for (int b = 0; b < 16; ++b) {
-            // byte b = channels 2b (low nibble) and 2b + 1 of the 32: codes 2b and 2b + 1
-            const uint32_t v = lut[(d[b >> 2] >> (8 * (b & 3))) & 255u];
-            const int bit = 12 * b, dw = bit >> 5, off = bit & 31;
-            o[dw] |= v << off;
-            if (off > 20) o[dw + 1] |= v >> (32 - off);
+        for (int i = 0; i < TILE_U; ++i) {
+            const uint32_t u = u0 + i * gridDim.x;
+            const uint32_t rb = u / KQ, q = u - rb * KQ;
+            const int64_t row0 = 32 * (int64_t)rb;
+            const int64_t nrows = R - row0 < 32 ? R - row0 : 32;
+            const bool ok = u < units && 4 * q + (c >> 1) < KS;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t *>(src) + (ok ? row0 * (K >> 1) : 0), (short)0,
+                ok && nrows > 0 ? (int)(nrows * (K >> 1)) : 0, 0x00020000);
+            d[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? r * (uint32_t)(K >> 1) + 128 * q + 16 * c : OOB, 0, 2);
         }
-        uint8_t *piece = dst + ((int64_t)rb * KS + ks) * PIECE;
-        *reinterpret_cast<v4u *>(piece + 16 * l) = v4u{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<v2u *>(piece + 1024 + 8 * l) = v2u{o[4], o[5]};
+#pragma unroll
+        for (int i = 0; i < TILE_U; ++i) {
+            const uint32_t u = u0 + i * gridDim.x;
+            const uint32_t rb = u / KQ, q = u - rb * KQ;
+            const uint32_t ks = 4 * q + (c >> 1);                // K-step of this thread's piece
+            if (u >= units || ks >= KS) continue;
+            v16f f[2];
+#pragma unroll
+            for (int b = 0; b < 16; ++b) {
+                const uint32_t w = d[i][b >> 2];
+                f[0][b] = (float)(int)__builtin_amdgcn_sbfe((int)w, 8 * (b & 3), 4);
+                f[1][b] = (float)(int)__builtin_amdgcn_sbfe((int)w, 8 * (b & 3) + 4, 4);
+            }
+            typedef unsigned v6u __attribute__((ext_vector_type(6)));
+            const v6u o = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(f[0], f[1], 1.0f);
+            uint8_t *piece = dst + ((int64_t)rb * KS + ks) * PIECE;
+            *reinterpret_cast<v4u *>(piece + 16 * l) = v4u{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<v2u *>(piece + 1024 + 8 * l) = v2u{o[4], o[5]};
+        }
     }
 }
 
@@ -539,7 +537,8 @@ hipError_t launch_tile_w4a4(const uint8_t *q, int64_t R, int K, uint8_t *out, hi
     if (K % 128) return hipErrorInvalidValue;
     const int64_t units = row_blocks(R) * ((K + 255) / 256);  // 32 rows x 256 channels each
     if (units >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-    const int64_t grid = units < cu_count() * 8 ? units : cu_count() * 8;
+    const int64_t want = (units + TILE_U - 1) / TILE_U;
+    const int64_t grid = want < cu_count() * 8 ? want : cu_count() * 8;
     hipLaunchKernelGGL(tile_fp6_kernel, dim3((unsigned)grid), dim3(256), 0, stream, q, out, R, K, (uint32_t)units);
     return hipGetLastError();
 }
