@@ -567,6 +567,17 @@ def test_linear_w4a4_x_given_matches_codes_path(cr, M, K, g, dtype):
     P.check_y(_x64(y_x), yown, "y (own codes)", strict_frac=1e-4)
 
 
+W4_WHOLE_TILE_CASES = [(1000, 4000, 512, 256), (1100, 8200, 512, 256), (1100, 8200, 384, 128)]
+
+
+@pytest.mark.parametrize("M,N,K,g", W4_WHOLE_TILE_CASES)
+def test_linear_w4a4_whole_tile_grids(cr, M, N, K, g):
+    """Ragged shapes whose grids take several rounds of the persistent walk (8 x 16 and 9 x 33
+    tiles of 256 x 128), against the oracle on the GPU's own codes and end to end."""
+    P.say("linear_w4a4 whole-tile grid M=%d N=%d K=%d g=%d" % (M, N, K, g))
+    _w4a4_case(cr, *workloads.ragged_case(M, K, N, seed=12), g)
+
+
 def _w4a4_case(cr, x, w, b, g):
     xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
     wq, ws = cr.prepare_weight(wd, g, 4)
