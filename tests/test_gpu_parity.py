@@ -541,6 +541,8 @@ def test_linear_w4a4_packed_matches(cr, M, N, K, g):
 
 
 FUSED_W4_CASES = [(M, K, g) for M in (1, 31, 33, 100) for K, g in ((256, 256), (384, 128), (2688, 128), (5376, 256))]
+# the largest K, and the largest K with a half 256-block at the end (group 128)
+FUSED_W4_CASES += [(33, 131072, 256), (40, 130944, 128)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
