@@ -10,7 +10,9 @@
 //   BITS = 4: one fp16 scale per (row, g-channel group) = max|group| / 7 with g = 256, or 128
 //             for a width 256 does not divide (section 四, detail 3, dynamic group), stored
 //             group-major ([K/g, rows]); two codes per byte with the even channel in the low nibble.
-// The same kernel prepares weights (rows = N) and quantizes activations (rows = M).
+// The same kernel prepares weights (rows = N) and quantizes activations (rows = M).  A second
+// kernel below (rotate_quant_fp6_kernel) computes the BITS = 4 codes and scales of activations the
+// same way and writes the codes straight in the FP6 matrix-core layout of the W4A4 GEMM.
 //
 // Data layout in registers.  A row is cut into "slots" of 256 consecutive channels.  Inside a
 // wavefront, lane bits 4:2 select one of 8 slots and the 8 lanes of a slot hold its 256
