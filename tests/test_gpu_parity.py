@@ -880,3 +880,21 @@ def test_split_k_gemm_runs_on_the_callers_stream_and_replays(cr):
     _replay_matches(lambda: cr.linear(None, wq, ws, b, xq=xq, x_scale=xs, out=y), y, ref)
     # rotate+quantize, the K-slices and the reduction in one graph
     _replay_matches(lambda: cr.linear(x, wq, ws, b, out=y), y, ref)
+
+
+def test_w4a4_linears_run_on_the_callers_stream_and_replay(cr):
+    """The W4A4 linear's kernels (rotate+quantize into FP6 tiles, the weight re-encode when the
+    weights are not pre-encoded, the GEMM) all go to the caller's stream and replay equal to eager,
+    at both scale groups."""
+    for M, N, K, g in ((100, 264, 768, 256), (33, 520, 384, 128)):
+        x, w, b = workloads.ragged_case(M, K, N, seed=13)
+        xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+        wq, ws = cr.prepare_weight(wd, g, 4)
+        wp = cr.pack_weight_w4a4(wq)
+        ref = cr.linear_w4a4(xd, wq, ws, bd, group=g).clone()
+        refp = cr.linear_w4a4_packed(xd, wp, ws, bd, group=g).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(ref, refp)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        _replay_matches(lambda: cr.linear_w4a4(xd, wq, ws, bd, group=g, out=y), y, ref)
+        _replay_matches(lambda: cr.linear_w4a4_packed(xd, wp, ws, bd, group=g, out=y), y, ref)
