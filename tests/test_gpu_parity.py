@@ -898,3 +898,33 @@ def test_w4a4_linears_run_on_the_callers_stream_and_replay(cr):
         y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
         _replay_matches(lambda: cr.linear_w4a4(xd, wq, ws, bd, group=g, out=y), y, ref)
         _replay_matches(lambda: cr.linear_w4a4_packed(xd, wp, ws, bd, group=g, out=y), y, ref)
+
+
+def test_linears_on_two_streams_at_once_match_sequential(cr):
+    """The library keeps no per-call state outside the caller's buffers (the no-allocation entry
+    point excepted): INT8 and W4A4 linears issued on two streams at the same time, each with its
+    own workspace, give the results of running them one after the other."""
+    M, N, K = 300, 2048, 1024
+    x1, w, b = workloads.ragged_case(M, K, N, seed=21)
+    x2, _, _ = workloads.ragged_case(M, K, N, seed=22)
+    x1, x2, wd, bd = x1.to(DEV), x2.to(DEV), w.to(DEV), b.to(DEV)
+    wq8, ws8 = cr.prepare_weight(wd, 256, 8)
+    wq4, ws4 = cr.prepare_weight(wd, 256, 4)
+    wp = cr.pack_weight_w4a4(wq4)
+    ref = [cr.linear(x1, wq8, ws8, bd).clone(), cr.linear_w4a4_packed(x2, wp, ws4, bd).clone(),
+           cr.linear(x2, wq8, ws8, bd).clone(), cr.linear_w4a4_packed(x1, wp, ws4, bd).clone()]
+    torch.cuda.synchronize()
+    outs = [torch.empty((M, N), dtype=torch.bfloat16, device=DEV) for _ in range(4)]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            cr.linear(x1, wq8, ws8, bd, out=outs[0])
+            cr.linear_w4a4_packed(x1, wp, ws4, bd, out=outs[3])
+        with torch.cuda.stream(s2):
+            cr.linear_w4a4_packed(x2, wp, ws4, bd, out=outs[1])
+            cr.linear(x2, wq8, ws8, bd, out=outs[2])
+    torch.cuda.synchronize()
+    for i in range(4):
+        assert torch.equal(outs[i], ref[i]), "output %d differs from the sequential run" % i
