@@ -13,8 +13,10 @@
 //    tiles; the tiles of each XCD form a contiguous range of the tile order, walked in groups
 //    along M so that the tiles running at the same time share their weight tile in that XCD's
 //    L2.  8 wavefronts (2 per SIMD, so one covers the other's waits) in 2(N) x 4(M) each own a
-//    128x64 sub-tile as 4x2 blocks of v_mfma_i32_32x32x32_i8 (128 int32 accumulators per lane,
-//    about 230 of the 256 registers a wave has at 2 waves per SIMD, with no spills);
+//    128x64 sub-tile as 8x4 blocks of v_mfma_i32_16x16x64_i8 (128 int32 accumulators per lane,
+//    255 of the 256 registers a wave has at 2 waves per SIMD, with no spills).  On gfx950 the
+//    16x16x64 form sustains more operations per second than the 32x32x32 one (4.4-4.5 against
+//    3.8 POP/s in register-only loops) for the same fragment bytes per operation;
 //  * K is streamed 128 bytes per K-tile through 2 LDS stages with buffer_load ... lds (global
 //    -> LDS, no VGPRs).  A row's K-tile is one whole 128-byte cache line and one load
 //    instruction moves 8 such lines, so every line is requested from L2 once (64-byte K-tiles
@@ -30,10 +32,9 @@
 //    reads of this stage (fragments are read one sub-step ahead) and the next K-tile, issued a
 //    whole K-tile earlier, has landed; the stage just read is then refilled with the K-tile
 //    after next;
-//  * the epilogue converts in registers and stores 16 bytes per lane straight to global memory
-//    (lane pairs exchange halves with v_permlane32_swap so each store covers 8 columns); the
-//    tile's sx/sw/bias are loaded into LDS with its first K-tile (4 rotating buffers: with short
-//    K the load side can run up to 3 tiles ahead);
+//  * the epilogue converts in registers, passes each 32-row block through LDS and stores whole
+//    rows of 256 bytes; the tile's sx/sw/bias are loaded into LDS with its first K-tile (4
+//    rotating buffers: with short K the load side can run up to 3 tiles ahead);
 //  * split-K tail: when the tiles leave the grid's last round badly under-filled, the tail tiles
 //    run as K-slices (the walk is over units: whole tiles, then slices), each slice storing its
 //    exact int32 sums to a workspace slot, and split_reduce_kernel sums the slots and applies
@@ -270,37 +271,44 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
         ld_kt = __builtin_amdgcn_readfirstlane(ld_kt + (real ? 1 : 0));
     };
 
-    // Fragment addressing: row = wave base + 32*blk + lane%32 (bases are multiples of 32, so
-    // swz(row) == swz(lane%32)); sub-step kk (0..3) reads K chunk 2*kk + lane/32.
-    const int frow = lane & 31, fhalf = lane >> 5;
+    // Fragment addressing (16x16x64 blocks): lane l supplies row (block base) + l%16 and the 16
+    // bytes of K chunk 4*kk + l/16 in K-step kk (0..1) of the K-tile; A and B use the same chunk
+    // for a lane, so every channel of the K-step meets its partner once.  Block bases are multiples
+    // of 16, so swz(row) == swz(l%16).
+    const int frow = lane & 15, fq = lane >> 4;
     const int arow = (wn * 128 + frow) * BK, brow = OPB + (wm * 64 + frow) * BK;
-    const int fpos[4] = {((0 + fhalf) ^ swz(frow)) * 16, ((2 + fhalf) ^ swz(frow)) * 16,
-                         ((4 + fhalf) ^ swz(frow)) * 16, ((6 + fhalf) ^ swz(frow)) * 16};
-    v4i fa[2][4], fb[2][2];
-    auto read_frags = [&](int g, int kk, int buf) {
-        const uint8_t *s0 = smem + (g & (NST - 1)) * STAGE + fpos[kk];
+    const int fpos[2] = {((0 + fq) ^ swz(frow)) * 16, ((4 + fq) ^ swz(frow)) * 16};
+    // fa[h]: weight blocks 4h..4h+3 of the K-step being worked on; fb[kk]: the 4 token blocks of
+    // K-step kk.  A K-tile runs as 4 sub-steps (kk, h) of 16 MFMAs each, in the order (0,0), (0,1),
+    // (1,0), (1,1); each sub-step reads the fragments the next one needs into the registers its
+    // predecessor has finished with.
+    v4i fa[2][4], fb[2][4];
+    auto read_a = [&](int g, int kk, int h) {
+        const uint8_t *s0 = smem + (g & (NST - 1)) * STAGE + fpos[kk] + arow;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) fa[buf][b] = *reinterpret_cast<const v4i *>(s0 + arow + 32 * b * BK);
-#pragma unroll
-        for (int b = 0; b < 2; ++b) fb[buf][b] = *reinterpret_cast<const v4i *>(s0 + brow + 32 * b * BK);
+        for (int b = 0; b < 4; ++b) fa[h][b] = *reinterpret_cast<const v4i *>(s0 + 16 * (4 * h + b) * BK);
     };
-    v16i acc[4][2];
+    auto read_b = [&](int g, int kk) {
+        const uint8_t *s0 = smem + (g & (NST - 1)) * STAGE + fpos[kk] + brow;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+        for (int b = 0; b < 4; ++b) fb[kk][b] = *reinterpret_cast<const v4i *>(s0 + 16 * b * BK);
+    };
+    v4i acc[8][4];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = v16i{};
-    auto mfma_range = [&](int buf, int j0, int j1) {
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = v4i{};
+    auto mfma_range = [&](int kk, int h, int j0, int j1) {
 #pragma unroll
         for (int j = j0; j < j1; ++j) {
-            const int bi = j >> 1, bj = j & 1;
-            acc[bi][bj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[buf][bi], fb[buf][bj], acc[bi][bj], 0, 0, 0);
+            const int bi = 4 * h + (j >> 2), bj = j & 3;
+            acc[bi][bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[h][j >> 2], fb[kk][bj], acc[bi][bj], 0, 0, 0);
         }
     };
-    auto mfmas = [&](int buf) { mfma_range(buf, 0, 8); };
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
-    // Accumulator layout of a 32x32 block (MFMA rows = weight rows n, columns = tokens m):
-    // lane holds m = lane%32 and, for register v, n = 8*(v/4) + 4*(lane/32) + v%4.
+    // Accumulator layout of a 16x16 block (MFMA rows = weight rows n, columns = tokens m):
+    // lane holds m = lane%16 and, for register v, n = 4*(lane/16) + v.
     // Stores go through a buffer descriptor per 32-row block (uniform, in SGPRs) with 32-bit
     // lane offsets; out-of-range rows/columns get an out-of-bounds offset and are dropped.  This
     // keeps the epilogue's register footprint small: a spill reload here would wait on vmcnt
@@ -322,35 +330,34 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
         const int m0 = J.tm * BM, n0 = J.tn * BN;
         const int Mi = p.M, Ni = p.N;
         // lane-dependent bases laundered so the addresses below are formed here, not hoisted out
-        // of the tile loop (where they would stay live through the main loop)
-        int erow = frow, ecol = wn * 128 + 4 * fhalf;
-        asm volatile("" : "+v"(erow), "+v"(ecol));
+        // of the tile loop (where they would stay live through the main loop): the lane's token
+        // row in a 16-row block and its first weight column in a 16-column block
+        int erow = frow, ecol = wn * 128 + 4 * fq, efq = fq;
+        asm volatile("" : "+v"(erow), "+v"(ecol), "+v"(efq));
         if constexpr (E == Epi::Int32) {
             issue_after_epilogue_reads(g);
 #pragma unroll
-            for (int bj = 0; bj < 2; ++bj) {
-                const int mr = m0 + wm * 64 + 32 * bj;            // first row of the block (uniform)
+            for (int bj = 0; bj < 4; ++bj) {
+                const int mr = m0 + wm * 64 + 16 * bj;            // first row of the block (uniform)
                 const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
                     static_cast<int32_t *>(p.y) + (int64_t)mr * p.N, (short)0, NUM_RECORDS, 0x00020000);
                 const bool rok = mr + erow < Mi;
 #pragma unroll
-                for (int bi = 0; bi < 4; ++bi)
+                for (int bi = 0; bi < 8; ++bi) {
+                    const int n = n0 + ecol + 16 * bi;
+                    const v4u d = {(unsigned)acc[bi][bj][0], (unsigned)acc[bi][bj][1], (unsigned)acc[bi][bj][2],
+                                   (unsigned)acc[bi][bj][3]};
+                    if (VEC || n + 3 < Ni) {
+                        const uint32_t off = (rok && n < Ni) ? (uint32_t)(erow * Ni + n) * 4u : OOB;
+                        __builtin_amdgcn_raw_buffer_store_b128(d, ry, off, 0, 0);
+                    } else {
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int n = n0 + ecol + 32 * bi + 8 * g;
-                        const v4u d = {(unsigned)acc[bi][bj][4 * g], (unsigned)acc[bi][bj][4 * g + 1],
-                                       (unsigned)acc[bi][bj][4 * g + 2], (unsigned)acc[bi][bj][4 * g + 3]};
-                        if (VEC || n + 3 < Ni) {
-                            const uint32_t off = (rok && n < Ni) ? (uint32_t)(erow * Ni + n) * 4u : OOB;
-                            __builtin_amdgcn_raw_buffer_store_b128(d, ry, off, 0, 0);
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const uint32_t off = (rok && n + e < Ni) ? (uint32_t)(erow * Ni + n + e) * 4u : OOB;
-                                __builtin_amdgcn_raw_buffer_store_b32(d[e], ry, off, 0, 0);
-                            }
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t off = (rok && n + e < Ni) ? (uint32_t)(erow * Ni + n + e) * 4u : OOB;
+                            __builtin_amdgcn_raw_buffer_store_b32(d[e], ry, off, 0, 0);
                         }
                     }
+                }
                 fence();
             }
         } else if (VEC && J.slot >= 0) {
@@ -361,71 +368,63 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
             int32_t *slot = p.part + (int64_t)J.slot * (BM * BN);
             // own laundered lane bases, so that no address of this branch is shared with (and kept
             // live across) the bf16 branch
-            int prow = frow, pcol = wn * 128 + 4 * fhalf;
+            int prow = frow, pcol = wn * 128 + 4 * fq;
             asm volatile("" : "+v"(prow), "+v"(pcol));
 #pragma unroll
-            for (int bj = 0; bj < 2; ++bj) {
-                const int ml = wm * 64 + 32 * bj;
+            for (int bj = 0; bj < 4; ++bj) {
+                const int ml = wm * 64 + 16 * bj;
                 const __amdgpu_buffer_rsrc_t rp =
                     __builtin_amdgcn_make_buffer_rsrc(slot + ml * BN, (short)0, NUM_RECORDS, 0x00020000);
                 const bool rok = m0 + ml + prow < Mi;
 #pragma unroll
-                for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int nl = pcol + 32 * bi + 8 * g;
-                        const v4u d = {(unsigned)acc[bi][bj][4 * g], (unsigned)acc[bi][bj][4 * g + 1],
-                                       (unsigned)acc[bi][bj][4 * g + 2], (unsigned)acc[bi][bj][4 * g + 3]};
-                        const uint32_t off = (rok && n0 + nl < Ni) ? (uint32_t)(prow * BN + nl) * 4u : OOB;
-                        __builtin_amdgcn_raw_buffer_store_b128(d, rp, off, 0, 0);
-                    }
+                for (int bi = 0; bi < 8; ++bi) {
+                    const int nl = pcol + 16 * bi;
+                    const v4u d = {(unsigned)acc[bi][bj][0], (unsigned)acc[bi][bj][1], (unsigned)acc[bi][bj][2],
+                                   (unsigned)acc[bi][bj][3]};
+                    const uint32_t off = (rok && n0 + nl < Ni) ? (uint32_t)(prow * BN + nl) * 4u : OOB;
+                    __builtin_amdgcn_raw_buffer_store_b128(d, rp, off, 0, 0);
+                }
                 fence();
             }
         } else if constexpr (VEC) {
             const float *ls = reinterpret_cast<const float *>(smem + SCALE_OFF + (j & (NSCALE - 1)) * SCALE_BYTES);
             // the wave's region: piece q (0..7) at 1024 w + 8192 (q & 3) (+ OPB for q >= 4); row r
             // of a 32-row block is piece r / 4 at (r % 4) * 256, its 16-byte chunk c at position
-            // c ^ (r % 16) (the 16 rows a write instruction's half-wave covers hit 16 bank groups)
+            // c ^ (r % 16).  A lane writes its 4 columns (8 bytes) of a 16x16 block as one half of
+            // a chunk: the 16 lanes of a column group cover 16 rows whose chunk positions differ,
+            // and the next 16 lanes the other halves, so each 32-lane write fills all 64 banks.
             uint8_t *reg = smem + (g & (NST - 1)) * STAGE + w * 1024;
             // lane-dependent parts, laundered so that they are formed here rather than hoisted
             // out of the tile loop (where they would stay live, or spill):
-            //   write side: row erow's base in the region and the XOR key of its chunk positions
+            //   write side: row erow's base in the region (rows erow and erow + 16 of the 32-row
+            //               block: + OPB), the XOR key of its chunk positions, and the lane's half
+            //               chunk: columns 4 fq .. 4 fq + 3 of a 16-column block are chunk
+            //               2 bi + fq / 2 of the row, half fq % 2
             //   read side:  instruction q reads row r = 4q + rrow, chunk rchunk, at position
             //               rchunk ^ (r % 16) = (rchunk ^ rrow) ^ 4 (q % 4)
-            int wrow = (erow >> 4) * OPB + 8192 * ((erow >> 2) & 3) + (erow & 3) * 256, wkey = fhalf ^ (erow & 15);
+            int wrow = 8192 * ((erow >> 2) & 3) + (erow & 3) * 256 + 8 * (efq & 1), wkey = (efq >> 1) ^ erow;
             int rrow = lane >> 4, rchunk = lane & 15, rkey = rchunk ^ (lane >> 4);
             asm volatile("" : "+v"(wrow), "+v"(wkey), "+v"(rrow), "+v"(rchunk), "+v"(rkey));
             const int n = n0 + wn * 128 + 8 * rchunk;
 #pragma unroll
-            for (int bj = 0; bj < 2; ++bj) {
-                const float sxm = ls[2 * BN + wm * 64 + 32 * bj + erow];
+            for (int bp = 0; bp < 2; ++bp) {
 #pragma unroll
-                for (int bi = 0; bi < 4; ++bi)
+                for (int b2 = 0; b2 < 2; ++b2) {
+                    const int bj = 2 * bp + b2;
+                    const float sxm = ls[2 * BN + wm * 64 + 16 * bj + erow];
 #pragma unroll
-                    for (int g2 = 0; g2 < 2; ++g2) {
-                        // column groups g = 2*g2 and 2*g2+1 of block bi: 4 columns each per lane
-                        uint32_t pk[2][2];
+                    for (int bi = 0; bi < 8; ++bi) {
+                        const int nl = ecol + 16 * bi;
+                        const v4f s4 = *reinterpret_cast<const v4f *>(ls + nl);
+                        const v4f b4 = *reinterpret_cast<const v4f *>(ls + BN + nl);
+                        float yv[4];
 #pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            const int gg = 2 * g2 + h;
-                            const int nl = ecol + 32 * bi + 8 * gg;
-                            const v4f s4 = *reinterpret_cast<const v4f *>(ls + nl);
-                            const v4f b4 = *reinterpret_cast<const v4f *>(ls + BN + nl);
-                            float yv[4];
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                yv[i] = __builtin_fmaf((float)acc[bi][bj][4 * gg + i], sxm * s4[i], b4[i]);
-                            pk[h][0] = pack_bf16x2(yv[0], yv[1]);
-                            pk[h][1] = pack_bf16x2(yv[2], yv[3]);
-                        }
-                        // lane l < 32 now holds columns 8g..8g+7 of group g = 2*g2, lane l+32 those
-                        // of group 2*g2+1 (same row m = l % 32): chunk 4 bi + 2 g2 + l / 32 of row m
-                        swap32(pk[0][0], pk[1][0]);
-                        swap32(pk[0][1], pk[1][1]);
-                        // chunk 4 bi + 2 g2 + fhalf of row erow, at position chunk ^ (erow % 16)
-                        *reinterpret_cast<v4u *>(reg + wrow + 16 * ((4 * bi + 2 * g2) ^ wkey)) =
-                            v4u{pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
+                        for (int i = 0; i < 4; ++i) yv[i] = __builtin_fmaf((float)acc[bi][bj][i], sxm * s4[i], b4[i]);
+                        // chunk 2 bi + fq / 2 of row erow + 16 b2, at position chunk ^ (erow % 16)
+                        *reinterpret_cast<v2u *>(reg + b2 * OPB + wrow + 16 * ((2 * bi) ^ wkey)) =
+                            v2u{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])};
                     }
+                }
                 // back in row order: instruction q reads rows 4q .. 4q+3, 16 lanes per row
                 v4u out[8];
 #pragma unroll
@@ -434,8 +433,8 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
                                                             16 * (rkey ^ (4 * (q & 3))));
                 // the loads of K-tile g + 2 refill the region: after the last block's reads, before
                 // its stores (the first barrier of the next job then waits for all but those 8)
-                if (bj == 1) issue_after_epilogue_reads(g);
-                const int mr = m0 + wm * 64 + 32 * bj;
+                if (bp == 1) issue_after_epilogue_reads(g);
+                const int mr = m0 + wm * 64 + 32 * bp;
                 const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
                     static_cast<uint16_t *>(p.y) + (int64_t)mr * p.N, (short)0, NUM_RECORDS, 0x00020000);
 #pragma unroll
@@ -450,48 +449,34 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
             issue_after_epilogue_reads(g);
             const float *ls = reinterpret_cast<const float *>(smem + SCALE_OFF + (j & (NSCALE - 1)) * SCALE_BYTES);
 #pragma unroll
-            for (int bj = 0; bj < 2; ++bj) {
-                const int mr = m0 + wm * 64 + 32 * bj;
+            for (int bj = 0; bj < 4; ++bj) {
+                const int mr = m0 + wm * 64 + 16 * bj;
                 const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
                     static_cast<uint16_t *>(p.y) + (int64_t)mr * p.N, (short)0, NUM_RECORDS, 0x00020000);
                 const bool rok = mr + erow < Mi;
-                const float sxm = ls[2 * BN + wm * 64 + 32 * bj + erow];
+                const float sxm = ls[2 * BN + wm * 64 + 16 * bj + erow];
 #pragma unroll
-                for (int bi = 0; bi < 4; ++bi)
+                for (int bi = 0; bi < 8; ++bi) {
+                    const int nl = ecol + 16 * bi;
+                    const v4f s4 = *reinterpret_cast<const v4f *>(ls + nl);
+                    const v4f b4 = *reinterpret_cast<const v4f *>(ls + BN + nl);
+                    const int n = n0 + nl;
+                    // rows not 16-byte aligned (N % 8 != 0): element stores, clipped at N
 #pragma unroll
-                    for (int g2 = 0; g2 < 2; ++g2) {
-                        uint32_t pk[2][2];
-#pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            const int gg = 2 * g2 + h;
-                            const int nl = ecol + 32 * bi + 8 * gg;
-                            const v4f s4 = *reinterpret_cast<const v4f *>(ls + nl);
-                            const v4f b4 = *reinterpret_cast<const v4f *>(ls + BN + nl);
-                            float yv[4];
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                yv[i] = __builtin_fmaf((float)acc[bi][bj][4 * gg + i], sxm * s4[i], b4[i]);
-                            pk[h][0] = pack_bf16x2(yv[0], yv[1]);
-                            pk[h][1] = pack_bf16x2(yv[2], yv[3]);
-                        }
-                        swap32(pk[0][0], pk[1][0]);
-                        swap32(pk[0][1], pk[1][1]);
-                        const int n = n0 + (ecol - 4 * fhalf) + 32 * bi + 8 * (2 * g2 + fhalf);
-                        // rows not 16-byte aligned (N % 8 != 0): element stores, clipped at N
-                        const uint32_t wv[4] = {pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const uint32_t off = (rok && n + e < Ni) ? (uint32_t)(erow * Ni + n + e) * 2u : OOB;
-                            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(wv[e >> 1] >> (16 * (e & 1))), ry, off, 0, 0);
-                        }
+                    for (int e = 0; e < 4; ++e) {
+                        const float yv = __builtin_fmaf((float)acc[bi][bj][e], sxm * s4[e], b4[e]);
+                        const uint32_t off = (rok && n + e < Ni) ? (uint32_t)(erow * Ni + n + e) * 2u : OOB;
+                        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16x2(yv, 0.0f) & 0xffffu), ry, off,
+                                                              0, 0);
                     }
+                }
                 fence();
             }
         }
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 8; ++a)
 #pragma unroll
-            for (int b = 0; b < 2; ++b) acc[a][b] = v16i{};
+            for (int b = 0; b < 4; ++b) acc[a][b] = v4i{};
     };
 
     if (njobs <= 0) return;
@@ -502,13 +487,14 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
     // Instruction interleaving inside one sub-step's scheduling region (sched_group_barrier masks:
     // 0x008 MFMA, 0x100 LDS read, 0x020 global read): the matrix pipe keeps its queue while the
     // fragment reads and the global loads go out between its instructions.
-    auto interleave_reads = [] {
+    // A sub-step has 16 MFMAs and issues 4 or 8 fragment reads, one after each of its first MFMAs.
+    auto interleave_reads = [](auto nreads) {
 #pragma unroll
-        for (int q = 0; q < 6; ++q) {
+        for (int q = 0; q < decltype(nreads)::value; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16 - decltype(nreads)::value, 0);
     };
     // prologue: K-tile 0 (and job 0's scales) visible, K-tile 1 in flight, first fragments
     next_job();
@@ -518,7 +504,8 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
     __syncthreads();
     issue_ktile(1, true);
     if (ld_kt == ld_ke) next_job();
-    read_frags(0, 0, 0);
+    read_a(0, 0, 0);
+    read_b(0, 0);
 
     int g = 0;
     for (int j = 0; j < njobs; ++j) {
@@ -530,23 +517,24 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
             nkt = __builtin_amdgcn_readfirstlane(J.ke - J.kb);
         }
         for (int kt = 0; kt < nkt; ++kt, ++g, first = 0) {
-            // sub-steps 0..2: MFMAs on the fragments read one sub-step earlier, the next
-            // sub-step's fragments read between them
-            read_frags(g, 1, 1);
-            mfmas(0);
-            interleave_reads();
+            // sub-steps (0,0), (0,1), (1,0): MFMAs on the fragments read one sub-step earlier, the
+            // next sub-step's fragments read between them
+            read_a(g, 0, 1);
+            mfma_range(0, 0, 0, 16);
+            interleave_reads(std::integral_constant<int, 4>{});
             fence();
-            read_frags(g, 2, 0);
-            mfmas(1);
-            interleave_reads();
+            read_a(g, 1, 0);
+            read_b(g, 1);
+            mfma_range(0, 1, 0, 16);
+            interleave_reads(std::integral_constant<int, 8>{});
             fence();
-            read_frags(g, 3, 1);
-            mfmas(0);
-            interleave_reads();
+            read_a(g, 1, 1);
+            mfma_range(1, 0, 0, 16);
+            interleave_reads(std::integral_constant<int, 4>{});
             fence();
-            // sub-step 3 starts before the barrier: these MFMAs use registers only, and keep the
+            // sub-step (1,1) starts before the barrier: these MFMAs use registers only, and keep the
             // matrix pipe busy while the wavefronts meet
-            mfma_range(1, 0, 2);
+            mfma_range(1, 1, 0, 4);
             fence();
             // K-tile g+1 must have landed before its first fragments are read: at most the
             // previous tile's epilogue stores may still be in flight right after an epilogue (and
@@ -557,22 +545,24 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
             // loads of K-tile g+1.  A raw barrier: the fence of __syncthreads() would make the
             // compiler wait for every store in flight as well.
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            // rest of sub-step 3: the loads of K-tile g+2 into the stage just freed and the first
+            // rest of sub-step (1,1): the loads of K-tile g+2 into the stage just freed and the first
             // fragments of K-tile g+1 go out between the MFMAs (past the end of the stream the
             // loads are out of range and the reads of a stale stage are never used).  After a
             // job's last K-tile the epilogue uses the freed stage first and issues the loads itself.
             issue_ktile(g, kt + 1 < nkt);
-            read_frags(g + 1, 0, 0);
-            mfma_range(1, 2, 8);
+            read_a(g + 1, 0, 0);
+            read_b(g + 1, 0);
+            mfma_range(1, 1, 4, 16);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
             fence();
             if (ld_kt == ld_ke) next_job();
             fence();
