@@ -89,8 +89,9 @@ def src_hash(*names) -> str:
 
 
 def traffic_from_profiles(key: str, current_hash: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken on the current
-    kernel source; otherwise None."""
+    """L2-miss bytes per launch (FETCH_SIZE + WRITE_SIZE scaled by a plain copy's counts, an upper
+    bound on HBM bytes) from the committed counter summary, if it was taken on the current kernel
+    source; otherwise None."""
     try:
         d = json.load(open(TRAFFIC_JSON))["kernels"].get(key)
     except (OSError, ValueError, KeyError):
