@@ -347,10 +347,11 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
                     const int n = n0 + ecol + 16 * bi;
                     const v4u d = {(unsigned)acc[bi][bj][0], (unsigned)acc[bi][bj][1], (unsigned)acc[bi][bj][2],
                                    (unsigned)acc[bi][bj][3]};
-                    if (VEC || n + 3 < Ni) {
+                    if constexpr (VEC) {
                         const uint32_t off = (rok && n < Ni) ? (uint32_t)(erow * Ni + n) * 4u : OOB;
                         __builtin_amdgcn_raw_buffer_store_b128(d, ry, off, 0, 0);
                     } else {
+                        // rows not 16-byte aligned (N % 8 != 0): element stores, clipped at N
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const uint32_t off = (rok && n + e < Ni) ? (uint32_t)(erow * Ni + n + e) * 4u : OOB;
@@ -736,8 +737,11 @@ hipError_t launch_gemm_i8(const int8_t *xq, const int8_t *wq, const float *sx, c
     // persistent grid: a multiple of 8 (XCD count) so virtual ids keep their XCD
     int grid = grid_capacity();
     if (U < grid) grid = (U + 7) & ~7;
-    if (epi == Epi::Int32)
+    // 16-byte stores of 4 (int32) or 8 (bf16) columns need N % 8 == 0; otherwise element stores
+    if (epi == Epi::Int32 && N % 8 == 0)
         hipLaunchKernelGGL((gemm_i8_kernel<Epi::Int32, true>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
+    else if (epi == Epi::Int32)
+        hipLaunchKernelGGL((gemm_i8_kernel<Epi::Int32, false>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
     else if (N % 8 == 0)
         hipLaunchKernelGGL((gemm_i8_kernel<Epi::Bf16, true>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
     else

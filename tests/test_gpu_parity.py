@@ -169,6 +169,8 @@ GEMM_CASES = [
     # M, N, K  (M <= 16 runs the decode GEMV kernel)
     (1, 64, 64), (12, 1000, 5120), (16, 264, 320), (12, 8192, 5120), (3, 5120, 25600),
     (17, 8, 64), (300, 264, 320), (513, 1000, 5376), (256, 256, 128), (1000, 1280, 1024),
+    # N % 8 != 0 (element stores; N % 4 != 0 too): GEMV and GEMM
+    (12, 1003, 5120), (17, 7, 64), (33, 1001, 320), (300, 262, 5376),
 ]
 
 
@@ -226,6 +228,8 @@ def test_linear_tiny_config(cr):
 LINEAR_CASES = [
     (12, 1000, 320, 64), (16, 1024, 5120, 256), (1, 200, 512, 256), (17, 264, 320, 32),
     (300, 1000, 768, 128), (257, 520, 1024, 256), (600, 264, 2688, 128),
+    # N % 8 != 0: the element-store epilogues of the GEMV and the GEMM
+    (12, 1001, 320, 64), (40, 1003, 512, 256), (257, 517, 1024, 256),
 ]
 
 
