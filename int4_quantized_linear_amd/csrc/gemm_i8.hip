@@ -33,8 +33,9 @@
 //    whole K-tile earlier, has landed; the stage just read is then refilled with the K-tile
 //    after next;
 //  * the epilogue converts in registers, passes each 32-row block through LDS and stores whole
-//    rows of 256 bytes; the tile's sx/sw/bias are loaded into LDS with its first K-tile (4
-//    rotating buffers: with short K the load side can run up to 3 tiles ahead);
+//    rows of 256 bytes (N % 8 == 0; element stores otherwise); the tile's sx/sw/bias are loaded
+//    into LDS with its first K-tile (4 rotating buffers: with short K the load side can run up
+//    to 3 tiles ahead);
 //  * split-K tail: when the tiles leave the grid's last round badly under-filled, the tail tiles
 //    run as K-slices (the walk is over units: whole tiles, then slices), each slice storing its
 //    exact int32 sums to a workspace slot, and split_reduce_kernel sums the slots and applies
@@ -309,18 +310,20 @@ __global__ void __launch_bounds__(NTHREADS, WG_PER_CU) gemm_i8_kernel(GemmParams
 
     // Accumulator layout of a 16x16 block (MFMA rows = weight rows n, columns = tokens m):
     // lane holds m = lane%16 and, for register v, n = 4*(lane/16) + v.
-    // Stores go through a buffer descriptor per 32-row block (uniform, in SGPRs) with 32-bit
-    // lane offsets; out-of-range rows/columns get an out-of-bounds offset and are dropped.  This
-    // keeps the epilogue's register footprint small: a spill reload here would wait on vmcnt
-    // and so drain every store and prefetch in flight.
+    // Stores go through a buffer descriptor per block of output rows (16, or 32 for the bf16
+    // 16-byte-store variant; uniform, in SGPRs) with 32-bit lane offsets; out-of-range
+    // rows/columns get an out-of-bounds offset and are dropped.  This keeps the epilogue's
+    // register footprint small: a spill reload here would wait on vmcnt and so drain every store
+    // and prefetch in flight.
     // The epilogue of a job runs after its last K-tile g.  It issues the loads of K-tile g + 2 (in
     // the K loop they go out during the last sub-step; for a job's last K-tile they wait until
-    // here) before any of its stores, so that the first barrier of the next job can leave the
-    // stores in flight.  The bf16 16-byte-store variant first passes each 32-row block through
-    // the wave's own 8 KiB of the LDS stage K-tile g occupied (every wave has read it: barrier of
-    // K-tile g) -- exactly the 8 pieces of 1 KiB this wave's loads of K-tile g + 2 refill, so no
-    // other wave touches them -- and writes whole 128-byte lines: 4 rows x 256 bytes per store
-    // instruction rather than 32 rows x 32 bytes, a quarter of the write transactions.
+    // here) before its stores (the bf16 16-byte-store variant: before its last row block's), so
+    // that the first barrier of the next job can leave those stores in flight.  That variant
+    // passes each 32-row block through the wave's own 8 KiB of the LDS stage K-tile g occupied
+    // (every wave has read it: barrier of K-tile g) -- exactly the 8 pieces of 1 KiB this wave's
+    // loads of K-tile g + 2 refill, so no other wave touches them -- and writes whole 128-byte
+    // lines: 4 rows x 256 bytes per store instruction rather than the 8-byte pieces of one row
+    // that each lane holds.
     auto issue_after_epilogue_reads = [&](int g) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // LDS reads of the region done
         issue_ktile(g, true);
