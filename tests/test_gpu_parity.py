@@ -170,7 +170,7 @@ GEMM_CASES = [
     (1, 64, 64), (12, 1000, 5120), (16, 264, 320), (12, 8192, 5120), (3, 5120, 25600),
     (17, 8, 64), (300, 264, 320), (513, 1000, 5376), (256, 256, 128), (1000, 1280, 1024),
     # N % 8 != 0 (element stores; N % 4 != 0 too): GEMV and GEMM
-    (12, 1003, 5120), (17, 7, 64), (33, 1001, 320), (300, 262, 5376),
+    (12, 1003, 5120), (12, 7, 320), (17, 7, 64), (33, 1001, 320), (300, 262, 5376),
     # the longest K the ABI takes (CONVROT_MAX_K): GEMV and GEMM
     (5, 40, 131072), (17, 72, 131072),
 ]
