@@ -40,7 +40,26 @@ struct RQParams {
     int ngroups;         // ceil(rows / rows_per_wg)
     float cg;            // 1/sqrt(g) in fp32
     double root;         // sqrt(g) in fp64
+    double rinv;         // 1/sqrt(g) in fp64
 };
+
+// Groups of at most 16 channels take each INT8 code from the correctly rounded fp32 quotient of
+// the normalised value by the scale, as the code's definition states, instead of from the
+// product with a rounded reciprocal.  Rotated sums of so few bf16 values carry few significant
+// bits, so exact half-integer quotients are frequent (0.03-0.05% of the codes of N(0, 0.02)
+// bf16 weight rows at g = 1 or 2), and the product's rounding breaks those ties either way.
+// Larger groups keep the single multiply: their ties are rare enough (~1e-6 of the codes).
+constexpr int EXACT_QUOTIENT_MAX_LG = 4;
+
+// Correctly rounded fp32 quotient v / s from m = RN(1 / s): q0 = RN(v m) is within an ulp of
+// v / s, the remainder v - q0 s is exact in one fma, and one correction step rounds correctly
+// (Markstein's theorem).  s == 0 comes with m == 0 and v == 0: the quotient is 0.
+__device__ __forceinline__ float quotient_rn(float v, float s, float m)
+{
+    const float q0 = v * m;
+    const float r = __builtin_fmaf(-q0, s, v);
+    return __builtin_fmaf(r, m, q0);
+}
 
 constexpr uint32_t OOB = 0x80000000u;   // buffer offset past num_records: loads read 0, stores drop
 
@@ -228,6 +247,7 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
         // sign left on this lane's values by the lane-exchange butterflies
         const float lsign = (((LG > 3 ? qd : 0) ^ (LG > 4 ? qd >> 1 : 0)) & 1) ? -1.0f : 1.0f;
         float mult[SETS][HS];
+        float scq[SETS], rcq[SETS];      // INT8 scale and its rounded reciprocal (exact-quotient codes)
         if constexpr (BITS == 8) {
             // row absmax across slots/waves through LDS (non-negative float bits order like uints).
             // smax[par] was cleared before the previous iteration's first barrier; the other
@@ -243,6 +263,8 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
                 const float amax = __uint_as_float(smax[par][rr[s] < 64 ? rr[s] : 63]);
                 const float sc = normalised(amax) / 127.0f;
                 mult[s][0] = sc > 0.0f ? lsign * (p.cg / sc) : 0.0f;
+                scq[s] = sc;
+                rcq[s] = sc > 0.0f ? 1.0f / sc : 0.0f;
                 if (ok[s] && jj[s] == 0 && qd == 0 && h == 0) static_cast<float *>(p.scale)[row0 + rr[s]] = sc;
             }
         } else {
@@ -275,7 +297,18 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
                 for (int r = 0; r < 4; ++r) {
                     uint32_t t[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) t[e] = rne_bits(v[s][r][e], mult[s][0]);
+                    for (int e = 0; e < 8; ++e) {
+                        if constexpr (LG <= EXACT_QUOTIENT_MAX_LG) {
+                            // the normalised value, rounded once to fp32: exact for even LG (a
+                            // signed power of two), through fp64 for odd LG
+                            float vn;
+                            if constexpr (LG % 2 == 0) vn = v[s][r][e] * (lsign * p.cg);
+                            else vn = (float)((double)v[s][r][e] * ((double)lsign * p.rinv));
+                            t[e] = rne_bits(quotient_rn(vn, scq[s], rcq[s]), 1.0f);
+                        } else {
+                            t[e] = rne_bits(v[s][r][e], mult[s][0]);
+                        }
+                    }
                     c[r][0] = pack4_i8(t[0], t[1], t[2], t[3]);
                     c[r][1] = pack4_i8(t[4], t[5], t[6], t[7]);
                 }
@@ -553,7 +586,8 @@ hipError_t launch_rotate_quant(const void *x, bool x_f32, int64_t rows, int K, i
     p.rows_per_wg = R;
     p.ngroups = (int)((rows + R - 1) / R);
     p.root = __builtin_sqrt((double)(1 << log2g));
-    p.cg = (float)(1.0 / p.root);
+    p.rinv = 1.0 / p.root;
+    p.cg = (float)p.rinv;
     static const int cus = [] {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
