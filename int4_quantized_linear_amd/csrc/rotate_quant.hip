@@ -41,24 +41,43 @@ struct RQParams {
     float cg;            // 1/sqrt(g) in fp32
     double root;         // sqrt(g) in fp64
     double rinv;         // 1/sqrt(g) in fp64
+    float cg_lo;         // fp32(1/sqrt(g) - cg): with cg, 1/sqrt(g) to ~48 bits
 };
 
-// Groups of at most 16 channels take each INT8 code from the correctly rounded fp32 quotient of
-// the normalised value by the scale, as the code's definition states, instead of from the
-// product with a rounded reciprocal.  Rotated sums of so few bf16 values carry few significant
-// bits, so exact half-integer quotients are frequent (0.03-0.05% of the codes of N(0, 0.02)
-// bf16 weight rows at g = 1 or 2), and the product's rounding breaks those ties either way.
-// Larger groups keep the single multiply: their ties are rare enough (~1e-6 of the codes).
-constexpr int EXACT_QUOTIENT_MAX_LG = 4;
+// The code is rint of the correctly rounded fp32 quotient of the normalised value v = fp32(vu /
+// sqrt(g)) by the stored scale s, as its definition states, not of a product with a rounded
+// reciprocal: rotated sums of bf16 values often carry few significant bits, so exact half-integer
+// quotients are common (3-5e-4 of the codes of N(0, 0.02) bf16 weight rows at g = 1 or 2, and of
+// small-integer activations at g = 256) and a rounded reciprocal breaks those ties either way.
+//
+// Quotient: m = RN(1 / s), q0 = RN(v m) is within an ulp of v / s, the remainder v - q0 s is
+// exact in one fma, and one correction step q0 + (v - q0 s) m rounds correctly (Markstein's
+// theorem).  For even log2 g, 1/sqrt(g) = cg is a power of two, folded into both factors
+// (a = sign cg m, b = s / (sign cg), exact scalings), so vu enters directly.  For odd log2 g, v is
+// vu cg + vu cg_lo in one fma, the correctly rounded product unless vu / sqrt(g) lies within
+// ~2^-47 of a rounding midpoint.  s == 0 comes with a = b = 0 and vu == 0: the code is 0.
+struct QuotientRN {
+    float a, b;
+};
 
-// Correctly rounded fp32 quotient v / s from m = RN(1 / s): q0 = RN(v m) is within an ulp of
-// v / s, the remainder v - q0 s is exact in one fma, and one correction step rounds correctly
-// (Markstein's theorem).  s == 0 comes with m == 0 and v == 0: the quotient is 0.
-__device__ __forceinline__ float quotient_rn(float v, float s, float m)
+template <int LG>
+__device__ __forceinline__ QuotientRN quotient_consts(float s, float sign, float cg)
 {
-    const float q0 = v * m;
-    const float r = __builtin_fmaf(-q0, s, v);
-    return __builtin_fmaf(r, m, q0);
+    const float m = s > 0.0f ? 1.0f / s : 0.0f;
+    if constexpr (LG % 2 == 0) return {m * (sign * cg), s > 0.0f ? s / (sign * cg) : 0.0f};
+    else return {m, s};
+}
+
+// fp32 of the quotient (before rint) for an unnormalised rotated value vu; chs = sign cg,
+// cls = sign cg_lo (odd log2 g only)
+template <int LG>
+__device__ __forceinline__ float quotient_rn(float vu, QuotientRN k, float chs, float cls)
+{
+    float v = vu;
+    if constexpr (LG % 2 != 0) v = __builtin_fmaf(vu, chs, vu * cls);
+    const float q0 = v * k.a;
+    const float r = __builtin_fmaf(-q0, k.b, v);
+    return __builtin_fmaf(r, k.a, q0);
 }
 
 constexpr uint32_t OOB = 0x80000000u;   // buffer offset past num_records: loads read 0, stores drop
@@ -135,7 +154,7 @@ __device__ __forceinline__ void fwht_slot(float (&v)[4][8], int qd)
 // are in flight while the other transforms; carrying the next row group's loads in registers
 // instead costs enough registers to halve that and is slower.
 template <bool F32IN, int BITS, int SETS, int LG>
-__global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
+__device__ __forceinline__ void rotate_quant_body(const RQParams &p)
 {
     __shared__ unsigned smax[2][64];
     const int lane = threadIdx.x & 63;
@@ -246,8 +265,8 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
         };
         // sign left on this lane's values by the lane-exchange butterflies
         const float lsign = (((LG > 3 ? qd : 0) ^ (LG > 4 ? qd >> 1 : 0)) & 1) ? -1.0f : 1.0f;
-        float mult[SETS][HS];
-        float scq[SETS], rcq[SETS];      // INT8 scale and its rounded reciprocal (exact-quotient codes)
+        QuotientRN qk[SETS][HS];
+        const float chs = lsign * p.cg, cls = lsign * p.cg_lo;
         if constexpr (BITS == 8) {
             // row absmax across slots/waves through LDS (non-negative float bits order like uints).
             // smax[par] was cleared before the previous iteration's first barrier; the other
@@ -262,9 +281,7 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
             for (int s = 0; s < SETS; ++s) {
                 const float amax = __uint_as_float(smax[par][rr[s] < 64 ? rr[s] : 63]);
                 const float sc = normalised(amax) / 127.0f;
-                mult[s][0] = sc > 0.0f ? lsign * (p.cg / sc) : 0.0f;
-                scq[s] = sc;
-                rcq[s] = sc > 0.0f ? 1.0f / sc : 0.0f;
+                qk[s][0] = quotient_consts<LG>(sc, lsign, p.cg);
                 if (ok[s] && jj[s] == 0 && qd == 0 && h == 0) static_cast<float *>(p.scale)[row0 + rr[s]] = sc;
             }
         } else {
@@ -277,7 +294,7 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
                     // one rounding to fp16 from the exact quotient (no double rounding through fp32)
                     const __half sh = f16_quotient_rne(normalised(m[s][hs]), 7.0f);
                     const float sc = __half2float(sh);
-                    mult[s][hs] = sc > 0.0f ? lsign * (p.cg / sc) : 0.0f;
+                    qk[s][hs] = quotient_consts<LG>(sc, lsign, p.cg);
                     const int64_t grp = (int64_t)jj[s] * HS + hs;
                     if (ok[s] && qd == 0 && h == 0 && grp * (256 / HS) < K)
                         static_cast<__half *>(p.scale)[grp * p.rows + row0 + rr[s]] = sh;
@@ -297,18 +314,7 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
                 for (int r = 0; r < 4; ++r) {
                     uint32_t t[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        if constexpr (LG <= EXACT_QUOTIENT_MAX_LG) {
-                            // the normalised value, rounded once to fp32: exact for even LG (a
-                            // signed power of two), through fp64 for odd LG
-                            float vn;
-                            if constexpr (LG % 2 == 0) vn = v[s][r][e] * (lsign * p.cg);
-                            else vn = (float)((double)v[s][r][e] * ((double)lsign * p.rinv));
-                            t[e] = rne_bits(quotient_rn(vn, scq[s], rcq[s]), 1.0f);
-                        } else {
-                            t[e] = rne_bits(v[s][r][e], mult[s][0]);
-                        }
-                    }
+                    for (int e = 0; e < 8; ++e) t[e] = rne_bits(quotient_rn<LG>(v[s][r][e], qk[s][0], chs, cls), 1.0f);
                     c[r][0] = pack4_i8(t[0], t[1], t[2], t[3]);
                     c[r][1] = pack4_i8(t[4], t[5], t[6], t[7]);
                 }
@@ -325,7 +331,8 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
                 for (int r = 0; r < 4; ++r) {
                     uint32_t t[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) t[e] = rne_bits(v[s][r][e], mult[s][r / (4 / HS)]);
+                    for (int e = 0; e < 8; ++e)
+                        t[e] = rne_bits(quotient_rn<LG>(v[s][r][e], qk[s][r / (4 / HS)], chs, cls), 1.0f);
                     c[r] = pack8_i4(t);
                 }
                 if constexpr (LG > 5) {
@@ -338,6 +345,21 @@ __global__ void __launch_bounds__(1024) rotate_quant_kernel(RQParams p)
             }
         }
     }
+}
+
+
+// One row slot set per wavefront (K <= 32768): two 16-wavefront workgroups per CU, so at most 64
+// VGPRs (8 wavefronts per SIMD).  More sets hold more of the row in registers and run with fewer.
+template <bool F32IN, int BITS, int SETS, int LG>
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) rotate_quant_kernel(RQParams p)
+{
+    rotate_quant_body<F32IN, BITS, SETS, LG>(p);
+}
+
+template <bool F32IN, int BITS, int SETS, int LG>
+__global__ void __launch_bounds__(1024) rotate_quant_wide_kernel(RQParams p)
+{
+    rotate_quant_body<F32IN, BITS, SETS, LG>(p);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -370,6 +392,7 @@ struct RQ6Params {
     int K;
     int nblk;            // ceil(K / 256)
     float cg;
+    float cg_lo;
     double root;
 };
 
@@ -427,7 +450,8 @@ __global__ void __launch_bounds__(256) rotate_quant_fp6_kernel(RQ6Params p)
     // per scale group: absmax over the slot's 8 lanes, fp16 scale, code multiplier (with the sign
     // the lane-exchange stages left on this lane)
     const float lsign = ((qd ^ (qd >> 1)) & 1) ? -1.0f : 1.0f;
-    float mult[HS];
+    QuotientRN qk[HS];
+    const float chs = lsign * p.cg, cls = lsign * p.cg_lo;
 #pragma unroll
     for (int hs = 0; hs < HS; ++hs) {
         float a = 0.0f;
@@ -443,7 +467,7 @@ __global__ void __launch_bounds__(256) rotate_quant_fp6_kernel(RQ6Params p)
         const float an = LG % 2 == 0 ? a * p.cg : (float)((double)a / p.root);
         const __half sh = f16_quotient_rne(an, 7.0f);
         const float sc = __half2float(sh);
-        mult[hs] = sc > 0.0f ? lsign * (p.cg / sc) : 0.0f;
+        qk[hs] = quotient_consts<LG>(sc, lsign, p.cg);
         const int64_t grp = (int64_t)j * HS + hs;
         if (rw < nrows && qd == 0 && h == 0 && grp * (256 / HS) < K) p.scale[grp * p.rows + row0 + rw] = sh;
     }
@@ -455,7 +479,8 @@ __global__ void __launch_bounds__(256) rotate_quant_fp6_kernel(RQ6Params p)
 #pragma unroll
     for (int pos = 0; pos < 32; ++pos) {
         const int r = (pos >> 4) | ((pos >> 2) & 2), e = pos & 7;
-        src[pos & 1][pos >> 1] = __builtin_fmaf(v[r][e], mult[r / (4 / HS)], kMagicRound) - kMagicRound;
+        src[pos & 1][pos >> 1] =
+            (quotient_rn<LG>(v[r][e], qk[r / (4 / HS)], chs, cls) + kMagicRound) - kMagicRound;
     }
     const v6u d = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(src[0], src[1], 1.0f);
     uint32_t dw[6] = {d[0], d[1], d[2], d[3], d[4], d[5]};
@@ -501,6 +526,7 @@ hipError_t launch_rotate_quant_fp6(const void *x, bool x_f32, int64_t rows, int 
     if (units >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     p.root = __builtin_sqrt((double)(1 << log2g));
     p.cg = (float)(1.0 / p.root);
+    p.cg_lo = (float)(1.0 / p.root - (double)p.cg);
     // one workgroup per unit: ~40 resident wavefronts per CU at this kernel's register count (a
     // persistent grid with the next unit's loads in flight holds fewer and is slower)
     const dim3 grid((unsigned)units), block(256);
@@ -537,19 +563,26 @@ static void rq_geometry(int64_t rows, int K, int &rows_per_wg, int &waves, int &
     }
 }
 
+template <bool F32, int B, int SS, int LG>
+static void rq_launch_one(dim3 grid, dim3 block, hipStream_t stream, const RQParams &p)
+{
+    if constexpr (SS == 1) hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, LG>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((rotate_quant_wide_kernel<F32, B, SS, LG>), grid, block, 0, stream, p);
+}
+
 template <bool F32, int B, int SS>
 static void rq_launch_lg(int log2g, dim3 grid, dim3 block, hipStream_t stream, const RQParams &p)
 {
     switch (log2g) {
-    case 0: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 0>), grid, block, 0, stream, p); break;
-    case 1: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 1>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 2>), grid, block, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 3>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 4>), grid, block, 0, stream, p); break;
-    case 5: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 5>), grid, block, 0, stream, p); break;
-    case 6: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 6>), grid, block, 0, stream, p); break;
-    case 7: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 7>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((rotate_quant_kernel<F32, B, SS, 8>), grid, block, 0, stream, p); break;
+    case 0: rq_launch_one<F32, B, SS, 0>(grid, block, stream, p); break;
+    case 1: rq_launch_one<F32, B, SS, 1>(grid, block, stream, p); break;
+    case 2: rq_launch_one<F32, B, SS, 2>(grid, block, stream, p); break;
+    case 3: rq_launch_one<F32, B, SS, 3>(grid, block, stream, p); break;
+    case 4: rq_launch_one<F32, B, SS, 4>(grid, block, stream, p); break;
+    case 5: rq_launch_one<F32, B, SS, 5>(grid, block, stream, p); break;
+    case 6: rq_launch_one<F32, B, SS, 6>(grid, block, stream, p); break;
+    case 7: rq_launch_one<F32, B, SS, 7>(grid, block, stream, p); break;
+    default: rq_launch_one<F32, B, SS, 8>(grid, block, stream, p); break;
     }
 }
 
@@ -565,9 +598,9 @@ static void rq_launch(int sets, int log2g, dim3 grid, dim3 block, hipStream_t st
 template <bool F32, int LG>
 static void rq_launch_i4(int sets, dim3 grid, dim3 block, hipStream_t stream, const RQParams &p)
 {
-    if (sets == 1) hipLaunchKernelGGL((rotate_quant_kernel<F32, 4, 1, LG>), grid, block, 0, stream, p);
-    else if (sets == 2) hipLaunchKernelGGL((rotate_quant_kernel<F32, 4, 2, LG>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((rotate_quant_kernel<F32, 4, 4, LG>), grid, block, 0, stream, p);
+    if (sets == 1) rq_launch_one<F32, 4, 1, LG>(grid, block, stream, p);
+    else if (sets == 2) rq_launch_one<F32, 4, 2, LG>(grid, block, stream, p);
+    else rq_launch_one<F32, 4, 4, LG>(grid, block, stream, p);
 }
 
 hipError_t launch_rotate_quant(const void *x, bool x_f32, int64_t rows, int K, int log2g, int bits, void *q,
@@ -588,6 +621,7 @@ hipError_t launch_rotate_quant(const void *x, bool x_f32, int64_t rows, int K, i
     p.root = __builtin_sqrt((double)(1 << log2g));
     p.rinv = 1.0 / p.root;
     p.cg = (float)p.rinv;
+    p.cg_lo = (float)(p.rinv - (double)p.cg);
     static const int cus = [] {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)

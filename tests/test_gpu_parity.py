@@ -80,8 +80,8 @@ def test_prepare_weight_bf16_rows_mismatch_rate_large_sample(cr, g):
     """bf16 N(0, 0.02) weight rows at every group, rule (a)'s rate with no allowance on 2.2M
     codes.  Small groups sum few bf16 values, so exact half-integer quotients are common there
     (a randomized shape sweep found 808 mismatches in 2.19M codes at g = 2 when those codes came
-    from a rounded reciprocal); groups of <= 16 channels now take the correctly rounded quotient
-    and are held to 1e-6 (only an inexact fp32 butterfly sum can still move a tie)."""
+    from a rounded reciprocal).  Codes are the rint of the correctly rounded quotient, so groups
+    of <= 16 channels, whose sums of bf16 values are exact in fp32, are held to 1e-6."""
     x, w, _ = workloads.ragged_case(10, 3584, 623, seed=2000 + g)
     wq, ws = cr.prepare_weight(w.to(DEV), g, 8)
     torch.cuda.synchronize()
@@ -89,6 +89,30 @@ def test_prepare_weight_bf16_rows_mismatch_rate_large_sample(cr, g):
     P.check_scales_f32(_np(ws), sr)
     n = P.check_codes(_np(wq), qr, "weight codes", rate=1e-6 if g <= 16 else P.CODE_MISMATCH_RATE, slack=False)
     P.say("bf16 weight rows g=%d: %d mismatches in %d codes" % (g, n, qr.size))
+
+
+@pytest.mark.parametrize("g", [1, 64, 128, 256])
+def test_quantize_small_integer_inputs_ties(cr, g):
+    """Integer-valued activations (|x| <= 3): the rotated values carry few significant bits, so
+    exact half-integer quotients are common at every group (an fp32 model of a code taken as the
+    product with a rounded reciprocal misses 6.7e-4 of them at g = 256).  The codes are the rint of
+    the correctly rounded quotient on both sides, so they must agree everywhere (1e-6 on 2M INT8
+    codes; INT4 at the groups it supports)."""
+    x = torch.from_numpy(np.random.default_rng(500 + g).integers(-3, 4, size=(512, 4096)).astype(np.float32))
+    xd = x.bfloat16().to(DEV)
+    q, s = cr.quantize_act(xd, group=g, bits=8)
+    torch.cuda.synchronize()
+    qr, sr = orc.quantize_act_i8(x.double().numpy(), g)
+    P.check_scales_f32(_np(s), sr)
+    n = P.check_codes(_np(q), qr, "int8 codes", rate=1e-6, slack=False)
+    P.say("small-integer inputs g=%d: %d INT8 mismatches in %d codes" % (g, n, qr.size))
+    if g in (128, 256):
+        q4, s4 = cr.quantize_act(xd, group=g, bits=4)
+        torch.cuda.synchronize()
+        c, sr4, _ = orc.prepare_i4(x.double().numpy(), g)
+        P.check_scales_f16(_np(s4).T, sr4, "fp16 scales", slack=False)
+        n4 = P.check_codes(orc.unpack_i4(_np(q4)), c, "int4 codes", rate=1e-6, slack=False)
+        P.say("small-integer inputs g=%d: %d INT4 mismatches in %d codes" % (g, n4, c.size))
 
 
 @pytest.mark.parametrize("g", [128, 256])
