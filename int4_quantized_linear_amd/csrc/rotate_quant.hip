@@ -52,10 +52,12 @@ struct RQParams {
 //
 // Quotient: m = RN(1 / s), q0 = RN(v m) is within an ulp of v / s, the remainder v - q0 s is
 // exact in one fma, and one correction step q0 + (v - q0 s) m rounds correctly (Markstein's
-// theorem).  For even log2 g, 1/sqrt(g) = cg is a power of two, folded into both factors
-// (a = sign cg m, b = s / (sign cg), exact scalings), so vu enters directly.  For odd log2 g, v is
-// vu cg + vu cg_lo in one fma, the correctly rounded product unless vu / sqrt(g) lies within
-// ~2^-47 of a rounding midpoint.  s == 0 comes with a = b = 0 and vu == 0: the code is 0.
+// theorem).  The sign the lane-exchange butterflies left on this lane's values goes into both
+// factors, and for even log2 g so does 1/sqrt(g) = cg, a power of two (a = sign cg m, b = s /
+// (sign cg): exact scalings), so the unnormalised sum vu enters directly.  For odd log2 g, the
+// normalised magnitude is vu cg + vu cg_lo in one fma, the correctly rounded product unless
+// vu / sqrt(g) lies within ~2^-47 of a rounding midpoint, with a = sign m, b = sign s.  s == 0
+// comes with a = b = 0 and vu == 0: the code is 0.
 struct QuotientRN {
     float a, b;
 };
@@ -65,16 +67,22 @@ __device__ __forceinline__ QuotientRN quotient_consts(float s, float sign, float
 {
     const float m = s > 0.0f ? 1.0f / s : 0.0f;
     if constexpr (LG % 2 == 0) return {m * (sign * cg), s > 0.0f ? s / (sign * cg) : 0.0f};
-    else return {m, s};
+    else return {sign * m, sign * s};
 }
 
-// fp32 of the quotient (before rint) for an unnormalised rotated value vu; chs = sign cg,
-// cls = sign cg_lo (odd log2 g only)
+// the scale s back from the constants (exact)
 template <int LG>
-__device__ __forceinline__ float quotient_rn(float vu, QuotientRN k, float chs, float cls)
+__device__ __forceinline__ float quotient_scale(QuotientRN k, float cg)
+{
+    return LG % 2 == 0 ? __builtin_fabsf(k.b) * cg : __builtin_fabsf(k.b);
+}
+
+// fp32 of the quotient (before rint) for an unnormalised rotated value vu
+template <int LG>
+__device__ __forceinline__ float quotient_rn(float vu, QuotientRN k, float cg, float cg_lo)
 {
     float v = vu;
-    if constexpr (LG % 2 != 0) v = __builtin_fmaf(vu, chs, vu * cls);
+    if constexpr (LG % 2 != 0) v = __builtin_fmaf(vu, cg, vu * cg_lo);
     const float q0 = v * k.a;
     const float r = __builtin_fmaf(-q0, k.b, v);
     return __builtin_fmaf(r, k.a, q0);
@@ -266,7 +274,6 @@ __device__ __forceinline__ void rotate_quant_body(const RQParams &p)
         // sign left on this lane's values by the lane-exchange butterflies
         const float lsign = (((LG > 3 ? qd : 0) ^ (LG > 4 ? qd >> 1 : 0)) & 1) ? -1.0f : 1.0f;
         QuotientRN qk[SETS][HS];
-        const float chs = lsign * p.cg, cls = lsign * p.cg_lo;
         if constexpr (BITS == 8) {
             // row absmax across slots/waves through LDS (non-negative float bits order like uints).
             // smax[par] was cleared before the previous iteration's first barrier; the other
@@ -310,11 +317,24 @@ __device__ __forceinline__ void rotate_quant_body(const RQParams &p)
         for (int s = 0; s < SETS; ++s) {
             if constexpr (BITS == 8) {
                 uint32_t c[4][2];
+                QuotientRN k = qk[s][0];
+                // the row's fp32 scale, exactly, from the constants; below 2^-100, 1/s can
+                // overflow, so such rows (numerically zero: max |v| < 127 * 2^-100) take v and s
+                // scaled by 2^64, which is exact and leaves every quotient as it is
+                const float sc = quotient_scale<LG>(k, p.cg);
+                const bool tiny = sc > 0.0f && sc < 0x1p-100f;
+                if (__builtin_amdgcn_ballot_w64(tiny) != 0 && tiny) {
+                    k = quotient_consts<LG>(sc * 0x1p64f, lsign, p.cg);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[s][r][e] *= 0x1p64f;
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     uint32_t t[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) t[e] = rne_bits(quotient_rn<LG>(v[s][r][e], qk[s][0], chs, cls), 1.0f);
+                    for (int e = 0; e < 8; ++e) t[e] = rne_bits(quotient_rn<LG>(v[s][r][e], k, p.cg, p.cg_lo), 1.0f);
                     c[r][0] = pack4_i8(t[0], t[1], t[2], t[3]);
                     c[r][1] = pack4_i8(t[4], t[5], t[6], t[7]);
                 }
@@ -332,7 +352,7 @@ __device__ __forceinline__ void rotate_quant_body(const RQParams &p)
                     uint32_t t[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        t[e] = rne_bits(quotient_rn<LG>(v[s][r][e], qk[s][r / (4 / HS)], chs, cls), 1.0f);
+                        t[e] = rne_bits(quotient_rn<LG>(v[s][r][e], qk[s][r / (4 / HS)], p.cg, p.cg_lo), 1.0f);
                     c[r] = pack8_i4(t);
                 }
                 if constexpr (LG > 5) {
@@ -451,7 +471,6 @@ __global__ void __launch_bounds__(256) rotate_quant_fp6_kernel(RQ6Params p)
     // the lane-exchange stages left on this lane)
     const float lsign = ((qd ^ (qd >> 1)) & 1) ? -1.0f : 1.0f;
     QuotientRN qk[HS];
-    const float chs = lsign * p.cg, cls = lsign * p.cg_lo;
 #pragma unroll
     for (int hs = 0; hs < HS; ++hs) {
         float a = 0.0f;
@@ -480,7 +499,7 @@ __global__ void __launch_bounds__(256) rotate_quant_fp6_kernel(RQ6Params p)
     for (int pos = 0; pos < 32; ++pos) {
         const int r = (pos >> 4) | ((pos >> 2) & 2), e = pos & 7;
         src[pos & 1][pos >> 1] =
-            (quotient_rn<LG>(v[r][e], qk[r / (4 / HS)], chs, cls) + kMagicRound) - kMagicRound;
+            (quotient_rn<LG>(v[r][e], qk[r / (4 / HS)], p.cg, p.cg_lo) + kMagicRound) - kMagicRound;
     }
     const v6u d = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(src[0], src[1], 1.0f);
     uint32_t dw[6] = {d[0], d[1], d[2], d[3], d[4], d[5]};

@@ -195,6 +195,33 @@ def test_quantize_zero_rows_and_single_outlier(cr):
     P.check_codes(_np(q), qr, rate=0.0)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("g", [128, 256])
+def test_quantize_tiny_rows(cr, g, dtype):
+    """Rows of tiny magnitude: an fp32 scale below 2^-100 (1/s would overflow past 2^-128) is
+    handled with v and s scaled by 2^64, exactly, so the codes are those of the same row at
+    ordinary magnitude and equal the oracle's."""
+    x, _, _ = workloads.ragged_case(8, 1024, 8, seed=31 + g)
+    x = x.float()
+    x[1] *= 2.0 ** -110          # scale near 2^-109
+    x[2] *= 2.0 ** -118          # scale near 2^-117
+    x[3] = 0.0
+    x[4] = 0.0
+    x[4, 7] = 2.0 ** -112        # one tiny value
+    x[5] *= 2.0 ** 100           # large, for contrast
+    x = x.to(dtype)
+    q, s = cr.quantize_act(x.to(DEV), group=g, bits=8)
+    torch.cuda.synchronize()
+    qr, sr = orc.quantize_act_i8(_x64(x), g)
+    P.check_scales_f32(_np(s), sr)
+    P.check_codes(_np(q), qr, "codes", rate=0.0)
+    # a row scaled by a power of two has the codes of the unscaled row
+    q0, _ = cr.quantize_act((x[0:1].float() * 2.0 ** -110).to(dtype).to(DEV), group=g, bits=8)
+    q1, _ = cr.quantize_act(x[0:1].to(DEV), group=g, bits=8)
+    torch.cuda.synchronize()
+    assert torch.equal(q0, q1)
+
+
 def test_prepare_weight_same_as_quantize_act(cr):
     w = workloads.gaussian_weights(300, 768, cfg=99)
     a = cr.prepare_weight(w.to(DEV), 256, 8)
@@ -255,7 +282,15 @@ def _linear_case(cr, x, w, b, g):
     P.check_scales_f32(_np(ws), ref["sw"], "sw")
     P.check_codes(_np(xq), ref["qx"], "qx")
     P.check_scales_f32(_np(xs), ref["sx"], "sx")
-    P.check_y(_x64(y), ref["y"])
+    # y against the oracle's dequant of the GPU's own codes (exact integer part; only fp32 and
+    # bf16 rounding differ) ...
+    bn = None if b is None else b.numpy()
+    yown = orc.dequant(orc.gemm_i32(_np(xq), _np(wq)), _np(xs), _np(ws), bn)
+    P.check_y(_x64(y), yown, "y (own codes)", strict_frac=1e-4)
+    # ... and rule (d) against the oracle end to end: a code that rule (a) lets differ moves a
+    # whole output row (an activation code) or column (a weight code) by one code step, so the
+    # element-wise bf16-ulp count is loose here, as in the W4A4 and W4A8 cases
+    P.check_y(_x64(y), ref["y"], "y (oracle codes)", strict_frac=2e-2)
     assert torch.equal(y, y2), "pre-quantized path differs from the fused path"
     return y, ref
 
