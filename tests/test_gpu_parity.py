@@ -1009,3 +1009,48 @@ def test_linears_on_two_streams_at_once_match_sequential(cr):
     torch.cuda.synchronize()
     for i in range(4):
         assert torch.equal(outs[i], ref[i]), "output %d differs from the sequential run" % i
+
+
+# ------------------------------------------------------------------ randomized legal shapes
+
+def _random_cases(n: int, seed: int):
+    """Seeded random shapes within each entry point's documented limits: INT8 at any power-of-two
+    group 1..256 and M across the GEMV/GEMM switch (ragged N), W4A4 and W4A8 at groups 128/256,
+    bf16 or fp32 x, with or without bias; sizes bounded so the oracle stays fast."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        path = ["w8a8", "w8a8", "w4a4", "w4a8"][int(rng.integers(0, 4))]
+        dtype = "bf16" if rng.random() < 0.7 else "f32"
+        if path == "w8a8":
+            g = int(2 ** rng.integers(0, 9))
+            K = max(g, 64) * int(rng.integers(1, max(2, 4096 // max(g, 64))))
+            M = int(rng.integers(1, 17)) if rng.random() < 0.5 else int(rng.integers(17, 600))
+            N = int(rng.integers(1, 1300))
+        elif path == "w4a4":
+            g = int(rng.choice([128, 256]))
+            K = g * int(rng.integers(max(1, 256 // g), 4096 // g))
+            M, N = int(rng.integers(1, 400)), 8 * int(rng.integers(1, 160))
+        else:
+            g = int(rng.choice([128, 256]))
+            K = g * int(rng.integers(1, 8192 // g))
+            M, N = int(rng.integers(1, 17)), 8 * int(rng.integers(1, 600))
+        while M * N * K > 1.2e8:
+            N = max(8, (N // 2) // 8 * 8)
+            M = max(1, M // 2)
+        cases.append((i, path, M, N, K, g, dtype, bool(rng.random() < 0.7)))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(48, 2024), ids=lambda c: "%d-%s-%dx%dx%d-g%d-%s%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], c[6], "-bias" if c[7] else ""))
+def test_random_legal_shapes(cr, case):
+    i, path, M, N, K, g, dtype, with_bias = case
+    P.say("random case %d: %s M=%d N=%d K=%d g=%d %s bias=%s" % (case[:7] + (with_bias,)))
+    x, w, b = workloads.ragged_case(M, K, N, seed=4000 + i, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    if path == "w8a8":
+        _linear_case(cr, x, w, b if with_bias else None, g)
+    elif path == "w4a4":
+        _w4a4_case(cr, x, w, b, g)
+    else:
+        _w4a8_case(cr, x, w, b if with_bias else None, "w4a8", g)
