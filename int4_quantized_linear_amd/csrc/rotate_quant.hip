@@ -467,8 +467,8 @@ __global__ void __launch_bounds__(256) rotate_quant_fp6_kernel(RQ6Params p)
 
     fwht_slot<LG>(v, qd);
 
-    // per scale group: absmax over the slot's 8 lanes, fp16 scale, code multiplier (with the sign
-    // the lane-exchange stages left on this lane)
+    // per scale group: absmax over the slot's 8 lanes, fp16 scale, the quotient's constants (with
+    // the sign the lane-exchange stages left on this lane); fp16 scales are >= 2^-24, so 1/s is finite
     const float lsign = ((qd ^ (qd >> 1)) & 1) ? -1.0f : 1.0f;
     QuotientRN qk[HS];
 #pragma unroll
@@ -491,7 +491,7 @@ __global__ void __launch_bounds__(256) rotate_quant_fp6_kernel(RQ6Params p)
         if (rw < nrows && qd == 0 && h == 0 && grp * (256 / HS) < K) p.scale[grp * p.rows + row0 + rw] = sh;
     }
 
-    // integer-valued codes (one rounding, as rne_bits) in the conversion's source order:
+    // integer-valued codes (rint of the correctly rounded quotient, as in the kernel above) in the conversion's source order:
     // output position 2i + b <- source b element i; positions 0..7 register 0, 8..15 register 2,
     // 16..23 register 1, 24..31 register 3
     v16f src[2];
