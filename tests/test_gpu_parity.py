@@ -1054,3 +1054,40 @@ def test_random_legal_shapes(cr, case):
         _w4a4_case(cr, x, w, b, g)
     else:
         _w4a8_case(cr, x, w, b if with_bias else None, "w4a8", g)
+
+
+def _structured_cases(n: int, seed: int):
+    """INT8 linears on structured activations: small integers (exact half-integer quotients are
+    common), a row of tiny magnitude (scale below 2^-100), a zero row; bf16 or fp32 x."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        kind = ["int", "tinyrow", "zerorow"][i % 3]
+        g = int(2 ** rng.integers(0, 9))
+        K = max(g, 64) * int(rng.integers(1, max(2, 4096 // max(g, 64))))
+        M = int(rng.integers(1, 17)) if rng.random() < 0.5 else int(rng.integers(17, 400))
+        N = int(rng.integers(1, 1100))
+        while M * N * K > 1.0e8:
+            N = max(1, N // 2)
+            M = max(1, M // 2)
+        cases.append((i, kind, M, N, K, g, "bf16" if rng.random() < 0.6 else "f32"))
+    return cases
+
+
+@pytest.mark.parametrize("case", _structured_cases(18, 77), ids=lambda c: "%d-%s-%dx%dx%d-g%d-%s" % c)
+def test_linear_structured_inputs(cr, case):
+    i, kind, M, N, K, g, dtype = case
+    P.say("structured case %d: %s M=%d N=%d K=%d g=%d %s" % case)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x, w, b = workloads.ragged_case(M, K, N, seed=5000 + i, dtype=dt)
+    rng = np.random.default_rng(6000 + i)
+    if kind == "int":
+        x = torch.from_numpy(rng.integers(-3, 4, size=(M, K)).astype(np.float32)).to(dt)
+    elif kind == "tinyrow":
+        x = x.float()
+        x[int(rng.integers(0, M))] *= 2.0 ** -112
+        x = x.to(dt)
+    else:
+        x = x.clone()
+        x[int(rng.integers(0, M))] = 0
+    _linear_case(cr, x, w, b, g)
